@@ -2,16 +2,12 @@
 
 The compute lives in the HIP/C++ shared library ``libsvdq.so`` built from
 ``csrc/`` (its C interface is ``include/svdq.h``). ``binding`` is a thin
-ctypes layer with the same entry-point names that marshals torch tensors and
-streams into that interface; it never computes anything itself and raises if
-the library is missing. ``workloads`` draws the seeded synthetic inputs.
+ctypes layer with the same entry-point names that marshals numpy arrays,
+torch tensors and streams into that interface; it never computes anything
+itself and raises if the library is missing. ``workloads`` draws the seeded
+synthetic inputs.
 """
 
+from . import binding, workloads  # noqa: F401
+
 __all__ = ["binding", "workloads"]
-
-
-def __getattr__(name):
-    if name == "binding":
-        from . import binding
-        return binding
-    raise AttributeError(name)

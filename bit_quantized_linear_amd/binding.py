@@ -1,0 +1,236 @@
+"""ctypes binding of libsvdq.so (interface: include/svdq.h).
+
+Argument marshalling only: host entry points take numpy arrays, device entry
+points take torch tensors resident on the GPU (their data pointers are passed
+through) and the current torch stream. Nothing here computes any step of the
+linear; if the library is missing every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsvdq.so")
+
+SVDQ_OK = 0
+SVDQ_ERR_INVALID_ARGUMENT = 1
+SVDQ_ERR_UNSUPPORTED_SHAPE = 2
+SVDQ_ERR_UNSUPPORTED_DEVICE = 3
+SVDQ_ERR_MISALIGNED = 4
+SVDQ_ERR_NUMERICAL = 5
+SVDQ_ERR_HIP = 6
+SVDQ_BF16 = 0
+SVDQ_F32 = 1
+GROUP = 64
+
+_vp, _i, _f, _sz = C.c_void_p, C.c_int, C.c_float, C.c_size_t
+
+# name -> (restype, argtypes), mirroring include/svdq.h
+SIGNATURES = {
+    "svdq_status_string": (C.c_char_p, [_i]),
+    "svdq_version": (_i, []),
+    "svdq_check_device": (_i, [_i]),
+    "svdq_prepare_weights": (_i, [_vp, _i, _i, _vp, _f, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "svdq_prepare_residual": (_i, [_vp, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp]),
+    "w8a8_prepare_weights": (_i, [_vp, _i, _i, _vp, _vp]),
+    "svdq_channel_absmax": (_i, [_vp, _i, _i, _vp, _vp]),
+    "svdq_quantize_act": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "svdq_w4a4_linear": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp]),
+    "w8a8_workspace_bytes": (_sz, [_i, _i]),
+    "w8a8_linear": (_i, [_vp, _vp, _f, _vp, _i, _i, _i, _vp, _sz, _vp, _vp]),
+    "svdq_debug_group_partials": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "w8a8_debug_acc": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
+    "svdq_debug_set_arch_override": (_i, [C.c_char_p]),
+}
+
+_lib = None
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+
+
+def lib():
+    """The loaded library; raises if it was not built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m bit_quantized_linear_amd.build` (there is no CPU fallback)")
+        handle = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().svdq_status_string(status).decode()
+
+
+def _check(fn, status):
+    if status != SVDQ_OK:
+        raise SvdqError(fn, status)
+
+
+def _np_ptr(a, dtype):
+    if a is None:
+        return None
+    if a.dtype != np.dtype(dtype) or not a.flags["C_CONTIGUOUS"]:
+        raise TypeError(f"expected a C-contiguous {np.dtype(dtype)} array")
+    return a.ctypes.data
+
+
+def _dev_ptr(t, itemsize=None):
+    """Device pointer of a torch tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise TypeError("device entry points take GPU tensors")
+    if not t.is_contiguous():
+        raise TypeError("tensors must be contiguous")
+    if itemsize is not None and t.element_size() != itemsize:
+        raise TypeError(f"expected {itemsize}-byte elements, got {t.element_size()}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ------------------------------------------------------------------ info --
+
+def svdq_version() -> int:
+    return lib().svdq_version()
+
+
+def svdq_check_device(device: int = 0) -> int:
+    return lib().svdq_check_device(device)
+
+
+def svdq_debug_set_arch_override(arch):
+    return lib().svdq_debug_set_arch_override(None if arch is None else arch.encode())
+
+
+# ------------------------------------------------------------------ host --
+
+def svdq_prepare_weights(W_bits, act_absmax, rank, alpha=0.5, group=GROUP, want_sigma=False):
+    """Host preparation. W_bits: uint16 [K, N] bf16 bits; act_absmax: float32 [K]."""
+    W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    act_absmax = np.ascontiguousarray(act_absmax, dtype=np.float32)
+    K, N = W_bits.shape
+    out = {
+        "s": np.empty(K, np.float32),
+        "l1t": np.empty((rank, K), np.uint16),
+        "l2t": np.empty((N, rank), np.uint16),
+        "qw": np.empty((N, K // 2), np.uint8),
+        "sw": np.empty((max(K // group, 0), N), np.float32),
+        "sigma": np.empty(rank, np.float64),
+    }
+    st = lib().svdq_prepare_weights(
+        _np_ptr(W_bits, np.uint16), K, N, _np_ptr(act_absmax, np.float32), float(alpha), rank, group,
+        out["s"].ctypes.data, out["l1t"].ctypes.data if rank else None,
+        out["l2t"].ctypes.data if rank else None, out["qw"].ctypes.data, out["sw"].ctypes.data,
+        out["sigma"].ctypes.data if rank else None)
+    _check("svdq_prepare_weights", st)
+    if not want_sigma:
+        out.pop("sigma")
+    return out
+
+
+def svdq_prepare_residual(W_bits, smooth, l1t, l2t, group=GROUP):
+    W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    smooth = np.ascontiguousarray(smooth, dtype=np.float32)
+    l1t = np.ascontiguousarray(l1t, dtype=np.uint16)
+    l2t = np.ascontiguousarray(l2t, dtype=np.uint16)
+    K, N = W_bits.shape
+    rank = l1t.shape[0]
+    qw = np.empty((N, K // 2), np.uint8)
+    sw = np.empty((K // group, N), np.float32)
+    st = lib().svdq_prepare_residual(_np_ptr(W_bits, np.uint16), K, N, _np_ptr(smooth, np.float32),
+                                     l1t.ctypes.data if rank else None, l2t.ctypes.data if rank else None,
+                                     rank, group, qw.ctypes.data, sw.ctypes.data)
+    _check("svdq_prepare_residual", st)
+    return {"qw": qw, "sw": sw}
+
+
+def w8a8_prepare_weights(W_bits):
+    W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    K, N = W_bits.shape
+    qw = np.empty((N, K), np.int8)
+    sw = np.zeros(1, np.float32)
+    st = lib().w8a8_prepare_weights(_np_ptr(W_bits, np.uint16), K, N, qw.ctypes.data, sw.ctypes.data)
+    _check("w8a8_prepare_weights", st)
+    return qw, float(sw[0])
+
+
+# ---------------------------------------------------------------- device --
+
+def svdq_channel_absmax(X, absmax, stream=None):
+    M, K = X.shape
+    st = lib().svdq_channel_absmax(_dev_ptr(X, 2), M, K, _dev_ptr(absmax, 4), _stream(stream))
+    _check("svdq_channel_absmax", st)
+
+
+def svdq_quantize_act(X, smooth, l1t, qx, sx, T, rank, group=GROUP, stream=None):
+    M, K = X.shape
+    st = lib().svdq_quantize_act(_dev_ptr(X, 2), _dev_ptr(smooth, 4), _dev_ptr(l1t, 2), M, K, rank,
+                                 group, _dev_ptr(qx, 1), _dev_ptr(sx, 4), _dev_ptr(T, 2), _stream(stream))
+    _check("svdq_quantize_act", st)
+
+
+def svdq_w4a4_linear(qx, sx, T, qw, sw, l2t, bias, Y, M, N, K, rank, group=GROUP, stream=None):
+    y_dtype = SVDQ_F32 if Y.element_size() == 4 else SVDQ_BF16
+    st = lib().svdq_w4a4_linear(_dev_ptr(qx, 1), _dev_ptr(sx, 4), _dev_ptr(T, 2), _dev_ptr(qw, 1),
+                                _dev_ptr(sw, 4), _dev_ptr(l2t, 2), _dev_ptr(bias, 2), M, N, K, rank,
+                                group, _dev_ptr(Y), y_dtype, _stream(stream))
+    _check("svdq_w4a4_linear", st)
+
+
+def w8a8_workspace_bytes(M, K) -> int:
+    return int(lib().w8a8_workspace_bytes(M, K))
+
+
+def w8a8_linear(X, qw, sw, bias, workspace, Y, stream=None):
+    M, K = X.shape
+    N = qw.shape[0]
+    st = lib().w8a8_linear(_dev_ptr(X, 2), _dev_ptr(qw, 1), float(sw), _dev_ptr(bias, 2), M, N, K,
+                           _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _dev_ptr(Y, 2), _stream(stream))
+    _check("w8a8_linear", st)
+
+
+def svdq_debug_group_partials(qx, qw, P, M, N, K, group=GROUP, stream=None):
+    st = lib().svdq_debug_group_partials(_dev_ptr(qx, 1), _dev_ptr(qw, 1), M, N, K, group,
+                                         _dev_ptr(P, 4), _stream(stream))
+    _check("svdq_debug_group_partials", st)
+
+
+def w8a8_debug_acc(qx, qw, acc, M, N, K, stream=None):
+    st = lib().w8a8_debug_acc(_dev_ptr(qx, 1), _dev_ptr(qw, 1), M, N, K, _dev_ptr(acc, 4),
+                              _stream(stream))
+    _check("w8a8_debug_acc", st)
+
+
+# ------------------------------------------------ convenience allocation --
+
+def w8a8_workspace_offset_codes() -> int:
+    """Byte offset of the int8 codes of X inside the w8a8 workspace."""
+    return 8192
+
+
+def w8a8_workspace_offset_scale() -> int:
+    """Byte offset of the fp32 activation scale inside the w8a8 workspace."""
+    return 4096

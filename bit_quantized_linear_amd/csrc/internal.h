@@ -1,0 +1,49 @@
+// Internal declarations shared by the C-ABI layer, the host preparation code
+// and the HIP kernel launchers of libsvdq.so. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "svdq.h"
+
+namespace svdq {
+
+// ---- host preparation (prepare.cpp) ----
+svdq_status prepare_weights_impl(const uint16_t *W, int K, int N,
+                                 const float *act_absmax, float alpha, int rank,
+                                 float *smooth, uint16_t *l1t, uint16_t *l2t,
+                                 uint8_t *qw, float *sw, double *sigma);
+svdq_status prepare_residual_impl(const uint16_t *W, int K, int N,
+                                  const float *smooth, const uint16_t *l1t,
+                                  const uint16_t *l2t, int rank, uint8_t *qw,
+                                  float *sw);
+svdq_status w8a8_prepare_impl(const uint16_t *W, int K, int N, int8_t *qw, float *sw);
+svdq_status truncated_svd(const double *A, int K, int N, int rank, double *U,
+                          double *S, double *V);
+bool all_finite_bf16(const uint16_t *p, int64_t n);
+
+// ---- device launchers (act_quant.hip, w4a4_gemm.hip, w8a8.hip) ----
+// Arguments are validated by the caller; launchers only pick a grid and launch.
+hipError_t launch_channel_absmax(const uint16_t *X, int M, int K, float *absmax,
+                                 hipStream_t stream);
+hipError_t launch_quantize_act(const uint16_t *X, const float *smooth,
+                               const uint16_t *l1t, int M, int K, int rank,
+                               uint8_t *qx, float *sx, uint16_t *T,
+                               hipStream_t stream);
+hipError_t launch_w4a4_linear(const uint8_t *qx, const float *sx,
+                              const uint16_t *T, const uint8_t *qw,
+                              const float *sw, const uint16_t *l2t,
+                              const uint16_t *bias, int M, int N, int K,
+                              int rank, void *Y, bool y_f32, hipStream_t stream);
+hipError_t launch_w4a4_partials(const uint8_t *qx, const uint8_t *qw, int M,
+                                int N, int K, int32_t *P, hipStream_t stream);
+hipError_t launch_w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
+                              const uint16_t *bias, int M, int N, int K,
+                              void *workspace, uint16_t *Y, hipStream_t stream);
+hipError_t launch_w8a8_acc(const int8_t *qx, const int8_t *qw, int M, int N,
+                           int K, int32_t *acc, hipStream_t stream);
+size_t w8a8_workspace_size(int M, int K);
+
+}  // namespace svdq

@@ -1,0 +1,418 @@
+// Host-side weight preparation for the SVDQuant W4A4 linear and the INT8
+// tensorwise W8A8 linear.
+//
+// Method sources (page title, passage):
+//  "Hugging Face встроила Nunchaku в Diffusers..." (iitog.ru), method
+//  paragraph: activation outliers are moved into the weights (smoothing), the
+//  hardest part of each weight is a 16-bit low-rank branch, the remainder is
+//  quantized to 4 bits.
+//  "SVDQuant ускоряет Krea 2 вдвое..." (ainews.so), "Решение: INT8 и W4A4":
+//  INT8 tensorwise weights; low-rank branches need no calibration dataset.
+//  "Diffusion Compiler" README, "Compiler" bullet: grouped INT4 weights.
+//
+// The truncated SVD is computed here without LAPACK: randomized block subspace
+// iteration (Halko, Martinsson & Tropp, SIAM Review 2011, Alg. 4.4) with
+// re-orthonormalization by classical Gram-Schmidt applied twice, followed by
+// a one-sided Jacobi SVD (Hestenes 1958) of the small projected matrix.
+// All of it is float64; only the stored factors are rounded to bf16.
+
+#include "svdq.h"
+#include "internal.h"
+
+#include <algorithm>
+#include <cfenv>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace svdq {
+
+namespace {
+
+// ---------------------------------------------------------------- threads --
+
+int host_threads() {
+    static int n = [] {
+        const char *env = std::getenv("SVDQ_HOST_THREADS");
+        int v = env ? std::atoi(env) : 0;
+        if (v <= 0) v = (int)std::thread::hardware_concurrency();
+        return std::max(1, std::min(v, 32));
+    }();
+    return n;
+}
+
+template <class F>
+void parallel_for(int64_t begin, int64_t end, F &&fn) {
+    int64_t total = end - begin;
+    if (total <= 0) return;
+    int nt = (int)std::min<int64_t>(host_threads(), total);
+    if (nt <= 1) {
+        fn(begin, end);
+        return;
+    }
+    std::vector<std::thread> pool;
+    pool.reserve(nt);
+    for (int t = 0; t < nt; ++t) {
+        int64_t a = begin + total * t / nt;
+        int64_t b = begin + total * (t + 1) / nt;
+        pool.emplace_back([&fn, a, b] { fn(a, b); });
+    }
+    for (auto &th : pool) th.join();
+}
+
+// ------------------------------------------------------------ conversions --
+
+inline float bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+inline bool bf16_is_finite(uint16_t b) { return (b & 0x7F80u) != 0x7F80u; }
+
+// Round a double to bfloat16 (8 significant bits), nearest-even, in a single
+// rounding. Normal range: quantum 2^(e-7) for 2^e <= |x| < 2^(e+1); below
+// bf16's smallest normal 2^-126 the quantum stays 2^-133.
+uint16_t f64_to_bf16(double x) {
+    if (x == 0.0 || !std::isfinite(x)) {
+        float f = (float)x;
+        uint32_t u;
+        std::memcpy(&u, &f, 4);
+        return (uint16_t)(u >> 16);
+    }
+    int e2;
+    std::frexp(x, &e2);  // x = m * 2^e2, 0.5 <= |m| < 1
+    int qexp = std::max(e2 - 8, -133);
+    double scaled = std::ldexp(x, -qexp);  // exact
+    double r = std::nearbyint(scaled);     // current mode: nearest-even
+    double y = std::ldexp(r, qexp);
+    const double bf16_max = (2.0 - std::ldexp(1.0, -7)) * std::ldexp(1.0, 127);
+    if (std::fabs(y) > bf16_max) y = std::copysign(INFINITY, y);
+    float f = (float)y;  // exact: y has at most 8 significant bits
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+// ------------------------------------------------------- dense kernels ---
+
+// Y[K x b] = A[K x N] * Z[N x b]
+void mul_AZ(const double *A, int K, int N, const double *Z, int b, double *Y) {
+    parallel_for(0, K, [&](int64_t k0, int64_t k1) {
+        std::vector<double> acc(b);
+        for (int64_t k = k0; k < k1; ++k) {
+            std::fill(acc.begin(), acc.end(), 0.0);
+            const double *a = A + k * (int64_t)N;
+            for (int n = 0; n < N; ++n) {
+                double w = a[n];
+                const double *z = Z + (int64_t)n * b;
+                for (int c = 0; c < b; ++c) acc[c] += w * z[c];
+            }
+            std::memcpy(Y + k * (int64_t)b, acc.data(), sizeof(double) * b);
+        }
+    });
+}
+
+// Z[N x b] = A^T[N x K] * Q[K x b]
+void mul_AtQ(const double *A, int K, int N, const double *Q, int b, double *Z) {
+    parallel_for(0, N, [&](int64_t n0, int64_t n1) {
+        int64_t w = n1 - n0;
+        std::vector<double> acc(w * b, 0.0);
+        for (int k = 0; k < K; ++k) {
+            const double *a = A + (int64_t)k * N + n0;
+            const double *q = Q + (int64_t)k * b;
+            for (int64_t i = 0; i < w; ++i) {
+                double v = a[i];
+                double *o = acc.data() + i * b;
+                for (int c = 0; c < b; ++c) o[c] += v * q[c];
+            }
+        }
+        std::memcpy(Z + n0 * (int64_t)b, acc.data(), sizeof(double) * w * b);
+    });
+}
+
+// Orthonormalize the b columns of V [rows x b] in place (classical
+// Gram-Schmidt, twice). A column that collapses is replaced by zeros.
+void orthonormalize(double *V, int64_t rows, int b) {
+    std::vector<double> col(rows), proj(b);
+    for (int j = 0; j < b; ++j) {
+        for (int64_t r = 0; r < rows; ++r) col[r] = V[r * b + j];
+        double norm0 = 0.0;
+        for (int64_t r = 0; r < rows; ++r) norm0 += col[r] * col[r];
+        norm0 = std::sqrt(norm0);
+        for (int pass = 0; pass < 2; ++pass) {
+            std::fill(proj.begin(), proj.end(), 0.0);
+            for (int64_t r = 0; r < rows; ++r) {
+                const double *row = V + r * b;
+                double c = col[r];
+                for (int i = 0; i < j; ++i) proj[i] += row[i] * c;
+            }
+            for (int64_t r = 0; r < rows; ++r) {
+                const double *row = V + r * b;
+                double s = 0.0;
+                for (int i = 0; i < j; ++i) s += row[i] * proj[i];
+                col[r] -= s;
+            }
+        }
+        double norm = 0.0;
+        for (int64_t r = 0; r < rows; ++r) norm += col[r] * col[r];
+        norm = std::sqrt(norm);
+        double inv = (norm > 1e-300 && norm > 1e-14 * norm0) ? 1.0 / norm : 0.0;
+        for (int64_t r = 0; r < rows; ++r) V[r * b + j] = col[r] * inv;
+    }
+}
+
+uint64_t splitmix64(uint64_t &s) {
+    uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// Standard normal draws (Box-Muller on splitmix64 uniforms).
+void gaussian_fill(double *out, int64_t n, uint64_t seed) {
+    uint64_t s = seed;
+    for (int64_t i = 0; i < n; i += 2) {
+        double u1 = ((splitmix64(s) >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+        double u2 = ((splitmix64(s) >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+        double rad = std::sqrt(-2.0 * std::log(u1));
+        out[i] = rad * std::cos(6.283185307179586 * u2);
+        if (i + 1 < n) out[i + 1] = rad * std::sin(6.283185307179586 * u2);
+    }
+}
+
+// One-sided Jacobi SVD of Z [rows x b]: rotates column pairs of Z until they
+// are mutually orthogonal, accumulating the rotations in J [b x b].
+// Returns false if the sweeps did not converge.
+bool one_sided_jacobi(double *Z, int64_t rows, int b, double *J) {
+    for (int i = 0; i < b; ++i)
+        for (int j = 0; j < b; ++j) J[i * b + j] = (i == j) ? 1.0 : 0.0;
+    const double tol = 1e-15;
+    for (int sweep = 0; sweep < 80; ++sweep) {
+        bool rotated = false;
+        for (int p = 0; p < b - 1; ++p) {
+            for (int q = p + 1; q < b; ++q) {
+                double alpha = 0.0, beta = 0.0, gamma = 0.0;
+                for (int64_t r = 0; r < rows; ++r) {
+                    double zp = Z[r * b + p], zq = Z[r * b + q];
+                    alpha += zp * zp;
+                    beta += zq * zq;
+                    gamma += zp * zq;
+                }
+                if (gamma == 0.0 || std::fabs(gamma) <= tol * std::sqrt(alpha * beta)) continue;
+                rotated = true;
+                double zeta = (beta - alpha) / (2.0 * gamma);
+                double t = std::copysign(1.0, zeta) / (std::fabs(zeta) + std::sqrt(1.0 + zeta * zeta));
+                double c = 1.0 / std::sqrt(1.0 + t * t);
+                double s = c * t;
+                for (int64_t r = 0; r < rows; ++r) {
+                    double zp = Z[r * b + p], zq = Z[r * b + q];
+                    Z[r * b + p] = c * zp - s * zq;
+                    Z[r * b + q] = s * zp + c * zq;
+                }
+                for (int r = 0; r < b; ++r) {
+                    double jp = J[r * b + p], jq = J[r * b + q];
+                    J[r * b + p] = c * jp - s * jq;
+                    J[r * b + q] = s * jp + c * jq;
+                }
+            }
+        }
+        if (!rotated) return true;
+    }
+    return false;
+}
+
+}  // namespace
+
+// Top-`rank` singular triplets of A [K x N] (float64, row-major).
+// U [K x rank], S [rank] (descending), V [N x rank].
+svdq_status truncated_svd(const double *A, int K, int N, int rank, double *U,
+                          double *S, double *V) {
+    const int full = std::min(K, N);
+    const int over = std::max(16, rank / 2);
+    const int b = std::min(full, rank + over);
+    const int iters = (b == full) ? 1 : 14;
+    std::vector<double> Q((int64_t)K * b), Z((int64_t)N * b);
+    gaussian_fill(Z.data(), (int64_t)N * b, 0x5EEDull + (uint64_t)K * 131 + N);
+    mul_AZ(A, K, N, Z.data(), b, Q.data());
+    orthonormalize(Q.data(), K, b);
+    for (int it = 0; it < iters; ++it) {
+        mul_AtQ(A, K, N, Q.data(), b, Z.data());
+        orthonormalize(Z.data(), N, b);
+        mul_AZ(A, K, N, Z.data(), b, Q.data());
+        orthonormalize(Q.data(), K, b);
+    }
+    // B^T = A^T Q  (N x b); Jacobi on its columns: B^T J = [sigma_i v_i]
+    mul_AtQ(A, K, N, Q.data(), b, Z.data());
+    std::vector<double> J((int64_t)b * b);
+    if (!one_sided_jacobi(Z.data(), N, b, J.data())) return SVDQ_ERR_NUMERICAL;
+    std::vector<double> sig(b);
+    for (int i = 0; i < b; ++i) {
+        double s2 = 0.0;
+        for (int64_t n = 0; n < N; ++n) s2 += Z[n * b + i] * Z[n * b + i];
+        sig[i] = std::sqrt(s2);
+    }
+    std::vector<int> order(b);
+    for (int i = 0; i < b; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return sig[x] > sig[y]; });
+    for (int i = 0; i < rank; ++i) {
+        int c = order[i];
+        double sv = sig[c];
+        if (!std::isfinite(sv)) return SVDQ_ERR_NUMERICAL;
+        S[i] = sv;
+        double inv = sv > 0 ? 1.0 / sv : 0.0;
+        for (int64_t n = 0; n < N; ++n) V[n * rank + i] = Z[n * b + c] * inv;
+        for (int64_t k = 0; k < K; ++k) {
+            double u = 0.0;
+            const double *q = Q.data() + k * b;
+            for (int j = 0; j < b; ++j) u += q[j] * J[(int64_t)j * b + c];
+            U[k * rank + i] = u;
+        }
+    }
+    return SVDQ_OK;
+}
+
+// INT4 symmetric group quantization of one column of R (stride `ld`), one
+// group of 64: A = max|r|, scale = A / 7 (fp32), q = clamp(rne(r / scale)).
+static void quantize_group_int4(const float *r, int64_t ld, int n, int8_t *q,
+                                float *scale) {
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) amax = std::max(amax, std::fabs(r[i * ld]));
+    float sc = amax / 7.0f;
+    *scale = sc;
+    if (sc == 0.0f) {
+        for (int i = 0; i < n; ++i) q[i] = 0;
+        return;
+    }
+    for (int i = 0; i < n; ++i) {
+        float quot = r[i * ld] / sc;
+        float v = std::nearbyint(quot);
+        v = std::min(7.0f, std::max(-7.0f, v));
+        q[i] = (int8_t)v;
+    }
+}
+
+svdq_status prepare_residual_impl(const uint16_t *W, int K, int N,
+                                  const float *smooth, const uint16_t *l1t,
+                                  const uint16_t *l2t, int rank, uint8_t *qw,
+                                  float *sw) {
+    const int G = K / SVDQ_GROUP;
+    // R as fp32 [K x N]
+    std::vector<float> R((int64_t)K * N);
+    std::vector<double> l1((int64_t)K * rank), l2((int64_t)rank * N);
+    for (int j = 0; j < rank; ++j)
+        for (int k = 0; k < K; ++k) l1[(int64_t)k * rank + j] = bf16_to_f32(l1t[(int64_t)j * K + k]);
+    for (int n = 0; n < N; ++n)
+        for (int j = 0; j < rank; ++j) l2[(int64_t)j * N + n] = bf16_to_f32(l2t[(int64_t)n * rank + j]);
+    parallel_for(0, K, [&](int64_t k0, int64_t k1) {
+        std::vector<double> d(N);
+        for (int64_t k = k0; k < k1; ++k) {
+            // D[k, :] summed over j in ascending order; each bf16 x bf16
+            // product is exact in float64
+            std::fill(d.begin(), d.end(), 0.0);
+            for (int j = 0; j < rank; ++j) {
+                double a = l1[k * rank + j];
+                const double *b = l2.data() + (int64_t)j * N;
+                for (int n = 0; n < N; ++n) d[n] = d[n] + a * b[n];
+            }
+            double s = smooth[k];
+            const uint16_t *wrow = W + k * (int64_t)N;
+            float *rrow = R.data() + k * (int64_t)N;
+            for (int n = 0; n < N; ++n) {
+                double diff = (double)bf16_to_f32(wrow[n]) - d[n];
+                rrow[n] = (float)(s * diff);
+            }
+        }
+    });
+    parallel_for(0, N, [&](int64_t n0, int64_t n1) {
+        std::vector<int8_t> codes(K);
+        for (int64_t n = n0; n < n1; ++n) {
+            for (int g = 0; g < G; ++g) {
+                float sc;
+                quantize_group_int4(R.data() + (int64_t)g * SVDQ_GROUP * N + n, N, SVDQ_GROUP,
+                                    codes.data() + g * SVDQ_GROUP, &sc);
+                sw[(int64_t)g * N + n] = sc;
+            }
+            uint8_t *row = qw + n * (int64_t)(K / 2);
+            for (int j = 0; j < K / 2; ++j) {
+                uint8_t lo = (uint8_t)(codes[2 * j] & 0xF);
+                uint8_t hi = (uint8_t)(codes[2 * j + 1] & 0xF);
+                row[j] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    });
+    return SVDQ_OK;
+}
+
+svdq_status prepare_weights_impl(const uint16_t *W, int K, int N,
+                                 const float *act_absmax, float alpha, int rank,
+                                 float *smooth, uint16_t *l1t, uint16_t *l2t,
+                                 uint8_t *qw, float *sw, double *sigma) {
+    // smoothing factors
+    const double a_exp = (double)alpha;
+    const double w_exp = 1.0 - (double)alpha;
+    for (int k = 0; k < K; ++k) {
+        double wmax = 0.0;
+        const uint16_t *row = W + (int64_t)k * N;
+        for (int n = 0; n < N; ++n) wmax = std::max(wmax, (double)std::fabs(bf16_to_f32(row[n])));
+        double a = act_absmax[k];
+        double s = 1.0;
+        if (a > 0.0 && wmax > 0.0) s = std::pow(a, a_exp) / std::pow(wmax, w_exp);
+        smooth[k] = (float)s;
+    }
+    if (rank > 0) {
+        std::vector<double> A((int64_t)K * N);
+        parallel_for(0, K, [&](int64_t k0, int64_t k1) {
+            for (int64_t k = k0; k < k1; ++k) {
+                double s = smooth[k];
+                for (int n = 0; n < N; ++n)
+                    A[k * (int64_t)N + n] = s * (double)bf16_to_f32(W[k * (int64_t)N + n]);
+            }
+        });
+        std::vector<double> U((int64_t)K * rank), S(rank), V((int64_t)N * rank);
+        svdq_status st = truncated_svd(A.data(), K, N, rank, U.data(), S.data(), V.data());
+        if (st != SVDQ_OK) return st;
+        for (int j = 0; j < rank; ++j) {
+            double root = std::sqrt(S[j]);
+            if (sigma) sigma[j] = S[j];
+            for (int k = 0; k < K; ++k)
+                l1t[(int64_t)j * K + k] = f64_to_bf16((U[(int64_t)k * rank + j] * root) / (double)smooth[k]);
+            for (int n = 0; n < N; ++n)
+                l2t[(int64_t)n * rank + j] = f64_to_bf16(root * V[(int64_t)n * rank + j]);
+        }
+    }
+    return prepare_residual_impl(W, K, N, smooth, l1t, l2t, rank, qw, sw);
+}
+
+svdq_status w8a8_prepare_impl(const uint16_t *W, int K, int N, int8_t *qw, float *sw) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < (int64_t)K * N; ++i) amax = std::max(amax, std::fabs(bf16_to_f32(W[i])));
+    float sc = amax / 127.0f;
+    *sw = sc;
+    parallel_for(0, N, [&](int64_t n0, int64_t n1) {
+        for (int64_t n = n0; n < n1; ++n) {
+            for (int k = 0; k < K; ++k) {
+                int8_t q = 0;
+                if (sc != 0.0f) {
+                    float v = std::nearbyint(bf16_to_f32(W[(int64_t)k * N + n]) / sc);
+                    v = std::min(127.0f, std::max(-127.0f, v));
+                    q = (int8_t)v;
+                }
+                qw[n * (int64_t)K + k] = q;
+            }
+        }
+    });
+    return SVDQ_OK;
+}
+
+bool all_finite_bf16(const uint16_t *p, int64_t n) {
+    for (int64_t i = 0; i < n; ++i)
+        if (!bf16_is_finite(p[i])) return false;
+    return true;
+}
+
+}  // namespace svdq

@@ -1,0 +1,238 @@
+/*
+ * svdq.h -- C interface of libsvdq.so: the SVDQuant W4A4 linear with its
+ * 16-bit low-rank branch, and the INT8 tensorwise W8A8 linear, for AMD
+ * Instinct MI355X (gfx950, CDNA4).
+ *
+ * The method (sources, cited by page title and passage):
+ *  [HF-SVDQ]   "Hugging Face встроила Nunchaku в Diffusers: диффузия быстрее на
+ *              30%, видеопамяти нужно до 50% меньше" (iitog.ru), method
+ *              paragraph: main layers run with 4-bit weights and 4-bit
+ *              activations; activation outliers are moved into the weights;
+ *              the hardest part of each weight matrix is a separate 16-bit
+ *              low-rank branch; the remainder is quantized to 4 bits.
+ *              "Nunchaku Lite" paragraph: such svdq_w4a4 layers replace the
+ *              attention and MLP projections (INT4 variant); hardware
+ *              paragraph: an unsupported GPU must be refused with a clear
+ *              error, never a wrong result.
+ *  [KREA-SVDQ] "SVDQuant ускоряет Krea 2 вдвое даже на старых NVIDIA GPU --
+ *              INT8/W4A4 вместо бесполезного FP8" (ainews.so), section
+ *              "Решение: INT8 и W4A4": INT8 tensorwise and W4A4 + SVDQuant,
+ *              low-rank branches compensating quantization error without a
+ *              calibration dataset.
+ *  [DC-README] "Diffusion Compiler" README (CodeAlexx/diffusion-compiler),
+ *              "Compiler" bullet: a grouped INT4 ("int4-group") physical
+ *              weight format.
+ *
+ *  y = dequant(Q4(X / s) . Q4(R)) + (X / s) . L1 . L2 + bias,
+ *  R = diag(s) W - L1 L2   (all on the stored bf16 factors).
+ *
+ * Conventions for every entry point
+ *  - Matrices are row-major. X is [M, K] (tokens x input features); the
+ *    weight W is [K, N] (y = X W); bf16 values travel as uint16_t bit
+ *    patterns.
+ *  - HOST entry points take host pointers, run synchronously on the calling
+ *    thread and touch no GPU.
+ *  - DEVICE entry points take device pointers (e.g. torch tensors' data),
+ *    enqueue kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *    return without synchronizing. The library never allocates, frees or
+ *    synchronizes device memory; the caller owns every buffer.
+ *  - Every check that can be made before a launch is made before the launch.
+ *    A failed check returns its status and launches nothing, so no output is
+ *    partially written. After launching, a HIP launch error is returned as
+ *    SVDQ_ERR_HIP.
+ *  - Device pointers must be 16-byte aligned (SVDQ_ERR_MISALIGNED).
+ *  - Only gfx950 is served: any other device gives
+ *    SVDQ_ERR_UNSUPPORTED_DEVICE before anything is launched.
+ *  - Calls on different streams may run concurrently; the library keeps no
+ *    mutable state apart from a per-device architecture cache.
+ *
+ * Packed INT4 layout (used by qx and qw): two's-complement nibbles, byte j of
+ * a row holds element k = 2j in its low nibble and k = 2j + 1 in its high
+ * nibble. Codes lie in [-7, 7] (symmetric grid; -8 never produced).
+ * Group scales are fp32, group size G = 64 along K, stored group-major.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum svdq_status {
+    SVDQ_OK = 0,
+    SVDQ_ERR_INVALID_ARGUMENT = 1,  /* null pointer, negative size, bad enum */
+    SVDQ_ERR_UNSUPPORTED_SHAPE = 2, /* K % 64, N % 8, rank range, group != 64 */
+    SVDQ_ERR_UNSUPPORTED_DEVICE = 3,/* no GPU, or not gfx950 */
+    SVDQ_ERR_MISALIGNED = 4,        /* device pointer not 16-byte aligned */
+    SVDQ_ERR_NUMERICAL = 5,         /* non-finite weight, SVD failed to converge */
+    SVDQ_ERR_HIP = 6                /* a HIP runtime call or launch failed */
+} svdq_status;
+
+typedef enum svdq_dtype {
+    SVDQ_BF16 = 0,
+    SVDQ_F32 = 1
+} svdq_dtype;
+
+#define SVDQ_GROUP 64
+#define SVDQ_MAX_RANK 64
+
+/* Text of a status code (static storage; never NULL). */
+const char *svdq_status_string(int status);
+
+/* Library ABI version (bumped on any signature or layout change). */
+int svdq_version(void);
+
+/* Fail-closed capability check [HF-SVDQ, hardware paragraph]: SVDQ_OK when
+ * `device` exists and is gfx950, SVDQ_ERR_UNSUPPORTED_DEVICE otherwise. */
+svdq_status svdq_check_device(int device);
+
+/* ---------------------------------------------------------------- HOST --- */
+
+/* Offline preparation of one SVDQuant weight [HF-SVDQ method; KREA-SVDQ
+ * "Решение"; DC-README int4-group]:
+ *   s_k = fp32(a_k^alpha / w_k^(1-alpha)), a_k = act_absmax[k],
+ *         w_k = max_n |W[k, n]|, s_k = 1 if a_k or w_k is 0;
+ *   W_hat = diag(s) W; its top-`rank` singular triplets (own subspace
+ *   iteration + Jacobi, float64) give L1s = bf16(diag(1/s) U_r Sigma_r^1/2)
+ *   and L2 = bf16(Sigma_r^1/2 V_r^T);
+ *   R = fp32(s_k (W - L1s L2)) and its INT4 group codes, as in
+ *   svdq_prepare_residual.
+ * In:  W [K, N] bf16 bits; act_absmax [K] (max |X| per input channel of
+ *      calibration activations, e.g. from svdq_channel_absmax); alpha in
+ *      [0, 1]; 0 <= rank <= min(64, K, N), rank % 16 == 0; group == 64;
+ *      K % 64 == 0, N % 8 == 0.
+ * Out: smooth [K] fp32; l1t [rank, K] bf16 bits (L1s transposed: one row per
+ *      rank component); l2t [N, rank] bf16 bits (L2 transposed: one row per
+ *      output column); qw [N, K/2] packed INT4 (one row per output column);
+ *      sw [K/64, N] fp32; sigma [rank] float64 (the singular values used) or
+ *      NULL. l1t/l2t may be NULL when rank == 0.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, NUMERICAL (non-finite W or
+ *      act_absmax, or the SVD did not converge). Outputs are undefined on
+ *      error. */
+svdq_status svdq_prepare_weights(const uint16_t *W, int K, int N,
+                                 const float *act_absmax, float alpha,
+                                 int rank, int group,
+                                 float *smooth, uint16_t *l1t, uint16_t *l2t,
+                                 uint8_t *qw, float *sw, double *sigma);
+
+/* The residual and weight-quantization half of svdq_prepare_weights, given
+ * smoothing factors and bf16 low-rank factors [HF-SVDQ method]:
+ *   D[k, n] = sum_{j=0}^{rank-1} L1s[k, j] L2[j, n]   (float64, j ascending)
+ *   R[k, n] = fp32(s_k * (W[k, n] - D[k, n]))          (float64, then fp32)
+ *   per output column n and K-group g: A = max |R|, sw = fp32(A / 7),
+ *   q = clamp(round-half-even(fp32(R / sw)), -7, 7); A == 0 -> sw = 0, q = 0.
+ * In:  W [K, N] bf16 bits; smooth [K]; l1t [rank, K]; l2t [N, rank].
+ * Out: qw [N, K/2] packed; sw [K/64, N].
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, NUMERICAL. */
+svdq_status svdq_prepare_residual(const uint16_t *W, int K, int N,
+                                  const float *smooth, const uint16_t *l1t,
+                                  const uint16_t *l2t, int rank, int group,
+                                  uint8_t *qw, float *sw);
+
+/* INT8 tensorwise weight preparation [KREA-SVDQ "Решение", INT8 tensorwise]:
+ *   sw = fp32(max |W| / 127); q = clamp(round-half-even(fp32(W / sw)),
+ *   -127, 127); all-zero W -> sw = 0, q = 0.
+ * In:  W [K, N] bf16 bits. Out: qw [N, K] int8 (one row per output column,
+ *      K contiguous); *sw. Errors: INVALID_ARGUMENT, NUMERICAL. */
+svdq_status w8a8_prepare_weights(const uint16_t *W, int K, int N,
+                                 int8_t *qw, float *sw);
+
+/* -------------------------------------------------------------- DEVICE --- */
+
+/* Calibration statistic for smoothing (self-calibration: the statistic comes
+ * from the activations themselves, no dataset) [HF-SVDQ method]:
+ *   absmax[k] = max(absmax[k], max_m |X[m, k]|)   (running maximum; the caller
+ *   zero-fills absmax before the first batch).
+ * In: X [M, K] bf16 (device). In/out: absmax [K] fp32 (device).
+ * Order-independent (integer max on the fp32 bit patterns): deterministic.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE (K % 8), MISALIGNED,
+ *      UNSUPPORTED_DEVICE, HIP. */
+svdq_status svdq_channel_absmax(const uint16_t *X, int M, int K, float *absmax,
+                                void *stream);
+
+/* Fused activation quantization -- one pass over X [HF-SVDQ method]:
+ *   X_hat = fp32(X / s_k)   (IEEE fp32 division, round to nearest even);
+ *   per row m and K-group g: A = max |X_hat|, sx[g, m] = fp32(A / 7),
+ *   qx = clamp(round-half-even(fp32(X_hat / sx)), -7, 7) packed to nibbles;
+ *   A == 0 -> sx = 0, codes 0;
+ *   T[m, :] = bf16(X[m, :] L1s)  -- the low-rank down-projection on raw X with
+ *   1/s folded into L1s, fp32 accumulation, one rounding to bf16.
+ * In:  X [M, K] bf16; smooth [K] fp32; l1t [rank, K] bf16 (NULL if rank 0).
+ * Out: qx [M, K/2] packed INT4; sx [K/64, M] fp32; T [M, rank] bf16 (NULL if
+ *      rank 0). M >= 0 (M == 0 launches nothing), K % 64 == 0,
+ *      rank % 16 == 0, rank <= 64, group == 64.
+ * Deterministic: T's partial sums are combined in a fixed order.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, MISALIGNED, UNSUPPORTED_DEVICE,
+ *      HIP. */
+svdq_status svdq_quantize_act(const uint16_t *X, const float *smooth,
+                              const uint16_t *l1t, int M, int K, int rank,
+                              int group, uint8_t *qx, float *sx, uint16_t *T,
+                              void *stream);
+
+/* The W4A4 linear with fused low-rank up-projection and bias
+ * [HF-SVDQ method and "Nunchaku Lite" paragraph]:
+ *   P[g, m, n] = sum_{k in g} qx[m, k] qw[n, k]      (exact integer, i8 MFMA)
+ *   acc[m, n]  = sum_g (sx[g, m] sw[g, n]) P[g, m, n] (fp32)
+ *   y[m, n]    = acc + sum_j T[m, j] L2[j, n] + bias[n]  (bf16 MFMA, fp32)
+ *   Y = y rounded once to bf16 (round to nearest even) or stored as fp32.
+ * In:  qx [M, K/2], sx [K/64, M], T [M, rank] (NULL if rank 0),
+ *      qw [N, K/2], sw [K/64, N], l2t [N, rank] (NULL if rank 0),
+ *      bias [N] bf16 or NULL. y_dtype: SVDQ_BF16 or SVDQ_F32.
+ * Out: Y [M, N] of y_dtype.
+ * Shapes: M >= 0, K % 64 == 0, N % 8 == 0, rank % 16 == 0, rank <= 64.
+ * Deterministic (no atomics; fixed summation order).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, MISALIGNED, UNSUPPORTED_DEVICE,
+ *      HIP. */
+svdq_status svdq_w4a4_linear(const uint8_t *qx, const float *sx,
+                             const uint16_t *T, const uint8_t *qw,
+                             const float *sw, const uint16_t *l2t,
+                             const uint16_t *bias, int M, int N, int K,
+                             int rank, int group, void *Y, int y_dtype,
+                             void *stream);
+
+/* Bytes of device workspace w8a8_linear needs for an [M, K] input. */
+size_t w8a8_workspace_bytes(int M, int K);
+
+/* INT8 tensorwise W8A8 linear [KREA-SVDQ "Решение", INT8 tensorwise]:
+ *   sx = fp32(max |X| / 127) over the whole X (computed on the device by an
+ *   order-independent max: deterministic); qx = clamp(round-half-even(
+ *   fp32(X / sx)), -127, 127) (all-zero X -> sx = 0, codes 0);
+ *   acc[m, n] = sum_k qx[m, k] qw[n, k]  (int32, all of K);
+ *   Y = bf16(fp32(acc) * fp32(sx * sw) + bias[n])  (round to nearest even).
+ * In:  X [M, K] bf16; qw [N, K] int8; sw (host value); bias [N] bf16 or NULL;
+ *      workspace of at least w8a8_workspace_bytes(M, K) bytes (device,
+ *      16-byte aligned; holds the int8 codes of X and the scale).
+ * Out: Y [M, N] bf16. Shapes: K % 64 == 0, N % 8 == 0, K * 127^2 < 2^31.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, MISALIGNED, UNSUPPORTED_DEVICE,
+ *      HIP. */
+svdq_status w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
+                        const uint16_t *bias, int M, int N, int K,
+                        void *workspace, size_t workspace_bytes, uint16_t *Y,
+                        void *stream);
+
+/* ------------------------------------------- TEST-ONLY (same kernels) --- */
+
+/* INT4 group partials from the W4A4 GEMM's own main loop:
+ *   P[g, m, n] = sum_{k in g} qx[m, k] qw[n, k]  as int32, [K/64, M, N]. */
+svdq_status svdq_debug_group_partials(const uint8_t *qx, const uint8_t *qw,
+                                      int M, int N, int K, int group,
+                                      int32_t *P, void *stream);
+
+/* INT8 accumulators from the W8A8 GEMM's own main loop:
+ *   acc[m, n] = sum_k qx[m, k] qw[n, k] as int32, [M, N]. */
+svdq_status w8a8_debug_acc(const int8_t *qx, const int8_t *qw, int M, int N,
+                           int K, int32_t *acc, void *stream);
+
+/* Test hook for the fail-closed path: when `arch` is non-NULL the device
+ * check sees that architecture name instead of the real one (NULL restores
+ * the real one). Host-only; never launches anything. */
+svdq_status svdq_debug_set_arch_override(const char *arch);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

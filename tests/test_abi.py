@@ -1,0 +1,130 @@
+"""The C-ABI library: it loads, exports every symbol its header declares, and
+fails closed on bad arguments and on a non-gfx950 device -- all checked
+without a GPU and without any compute call (rejected calls launch nothing)."""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_quantized_linear_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below is rejected first
+MISALIGNED = 0x10008
+
+
+def header_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_0-9]+)\s*\(", text)
+    keep = [n for n in names if n.startswith(("svdq_", "w8a8_"))]
+    return sorted(set(keep))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = C.CDLL(b.LIB_PATH)
+    names = header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(b.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings_and_version():
+    assert b.svdq_version() == 1
+    for s in range(7):
+        assert b.status_string(s)
+    assert "unknown" in b.status_string(99)
+
+
+def test_no_gpu_means_unsupported_device():
+    # in a container without a GPU the capability check fails closed
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert b.svdq_check_device(0) == b.SVDQ_ERR_UNSUPPORTED_DEVICE
+
+
+def test_arch_override_fails_closed_before_launch():
+    lib = b.lib()
+    b.svdq_debug_set_arch_override("gfx942")
+    try:
+        st = lib.svdq_quantize_act(FAKE, FAKE, FAKE, 16, 128, 16, 64, FAKE, FAKE, FAKE, None)
+        assert st == b.SVDQ_ERR_UNSUPPORTED_DEVICE
+        st = lib.svdq_w4a4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 64, 128, 16, 64,
+                                  FAKE, b.SVDQ_BF16, None)
+        assert st == b.SVDQ_ERR_UNSUPPORTED_DEVICE
+        st = lib.w8a8_linear(FAKE, FAKE, 1.0, None, 16, 64, 128, FAKE, 1 << 20, FAKE, None)
+        assert st == b.SVDQ_ERR_UNSUPPORTED_DEVICE
+    finally:
+        b.svdq_debug_set_arch_override(None)
+
+
+@pytest.mark.parametrize("args,expected", [
+    # (M, K, rank, group) -> status
+    ((16, 100, 16, 64), b.SVDQ_ERR_UNSUPPORTED_SHAPE),   # K % 64
+    ((16, 128, 16, 32), b.SVDQ_ERR_UNSUPPORTED_SHAPE),   # group != 64
+    ((16, 128, 24, 64), b.SVDQ_ERR_UNSUPPORTED_SHAPE),   # rank % 16
+    ((16, 128, 80, 64), b.SVDQ_ERR_UNSUPPORTED_SHAPE),   # rank > 64
+    ((-1, 128, 16, 64), b.SVDQ_ERR_INVALID_ARGUMENT),    # negative M
+    ((16, 0, 16, 64), b.SVDQ_ERR_INVALID_ARGUMENT),      # K == 0
+])
+def test_quantize_act_shape_checks(args, expected):
+    M, K, rank, group = args
+    st = b.lib().svdq_quantize_act(FAKE, FAKE, FAKE, M, K, rank, group, FAKE, FAKE, FAKE, None)
+    assert st == expected
+
+
+def test_null_and_misaligned_pointers_rejected():
+    lib = b.lib()
+    assert lib.svdq_quantize_act(None, FAKE, FAKE, 16, 128, 16, 64, FAKE, FAKE, FAKE, None) == \
+        b.SVDQ_ERR_INVALID_ARGUMENT
+    assert lib.svdq_quantize_act(MISALIGNED, FAKE, FAKE, 16, 128, 16, 64, FAKE, FAKE, FAKE, None) == \
+        b.SVDQ_ERR_MISALIGNED
+    assert lib.svdq_w4a4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 60, 128, 16, 64, FAKE,
+                                b.SVDQ_BF16, None) == b.SVDQ_ERR_UNSUPPORTED_SHAPE  # N % 8
+    assert lib.svdq_w4a4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 64, 128, 16, 64, FAKE,
+                                7, None) == b.SVDQ_ERR_INVALID_ARGUMENT  # dtype
+    assert lib.svdq_w4a4_linear(FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 16, 64, 128, 16, 64, FAKE,
+                                b.SVDQ_BF16, None) == b.SVDQ_ERR_INVALID_ARGUMENT  # T missing
+    assert lib.w8a8_linear(FAKE, FAKE, 1.0, None, 16, 64, 128, FAKE, 16, FAKE, None) == \
+        b.SVDQ_ERR_INVALID_ARGUMENT  # workspace too small
+    assert lib.w8a8_linear(FAKE, FAKE, float("nan"), None, 16, 64, 128, FAKE, 1 << 20, FAKE, None) == \
+        b.SVDQ_ERR_INVALID_ARGUMENT
+    assert lib.w8a8_linear(FAKE, FAKE, 1.0, None, 16, 64, 133184, FAKE, 1 << 40, FAKE, None) == \
+        b.SVDQ_ERR_UNSUPPORTED_SHAPE  # K 127^2 overflows int32
+    assert lib.svdq_debug_group_partials(FAKE, FAKE, 16, 64, 96, 64, FAKE, None) == \
+        b.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert lib.svdq_channel_absmax(FAKE, 4, 12, FAKE, None) == b.SVDQ_ERR_UNSUPPORTED_SHAPE
+
+
+def test_workspace_size_covers_codes():
+    assert b.w8a8_workspace_bytes(4608, 3072) >= 4608 * 3072 + b.w8a8_workspace_offset_codes()
+    assert b.w8a8_workspace_bytes(-1, 64) == 0
+
+
+def test_host_prepare_rejects_bad_input():
+    W = np.zeros((128, 64), np.uint16)
+    a = np.ones(128, np.float32)
+    with pytest.raises(b.SvdqError) as e:
+        b.svdq_prepare_weights(W[:100], a[:100], 16)
+    assert e.value.status == b.SVDQ_ERR_UNSUPPORTED_SHAPE
+    with pytest.raises(b.SvdqError) as e:
+        b.svdq_prepare_weights(W, a, 80)
+    assert e.value.status == b.SVDQ_ERR_UNSUPPORTED_SHAPE
+    Wn = W.copy()
+    Wn[3, 5] = 0x7FC0  # NaN
+    with pytest.raises(b.SvdqError) as e:
+        b.svdq_prepare_weights(Wn, a, 16)
+    assert e.value.status == b.SVDQ_ERR_NUMERICAL
+    a2 = a.copy()
+    a2[0] = np.inf
+    with pytest.raises(b.SvdqError) as e:
+        b.svdq_prepare_weights(W, a2, 16)
+    assert e.value.status == b.SVDQ_ERR_NUMERICAL

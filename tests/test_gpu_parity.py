@@ -1,0 +1,318 @@
+"""HIP path vs the CPU oracle, through the C-ABI (needs an MI355X).
+
+Bars: packed INT4 codes, INT8 codes, group scales and int32 partials /
+accumulators bit-exact; T within one bf16 ulp per element and rel-L2 <= 1e-3;
+outputs rel-L2 <= 1e-3, cosine >= 0.99999 and all finite. Inputs are prepared
+by the oracle and handed to the library; nothing flows back into the oracle.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from bit_quantized_linear_amd import binding as b
+from bit_quantized_linear_amd import workloads as wl
+from oracle import svdquant as sq
+from oracle import w8a8 as o8
+from tests import gpu_harness as H
+from tests.oracle_pins import cosine, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+F64 = np.float64
+REL_L2 = 1e-3
+COS = 0.99999
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert b.svdq_check_device(torch.cuda.current_device()) == b.SVDQ_OK, "not a gfx950 device"
+
+
+def check_T(T_gpu, T_ref):
+    Th = T_gpu if isinstance(T_gpu, np.ndarray) else H.host(T_gpu)
+    got = sq.bf16_from_bits(Th.view(np.uint16))
+    ref = np.asarray(T_ref, dtype=F64)
+    # at most one bf16 ulp apart where the fp32 sum straddles a rounding point
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(ref), 1e-30))[1] - 8)
+    assert np.all(np.abs(got - ref) <= ulp + 1e-30)
+    assert rel_l2(got, ref) <= REL_L2
+    return got
+
+
+def check_output(y, ref):
+    assert np.all(np.isfinite(y))
+    assert rel_l2(y, ref) <= REL_L2, rel_l2(y, ref)
+    assert cosine(y, ref) >= COS, cosine(y, ref)
+
+
+# ------------------------------------------------------------ act quant --
+
+@pytest.mark.parametrize("shape", [(64, 256, 16), (77, 320, 32), (1, 64, 16), (130, 128, 0), (33, 192, 64)])
+def test_quantize_act_small(shape):
+    M, K, rank = shape
+    say("quantize_act", shape)
+    p = H.make_problem(M, K, max(rank, 16) * 2 if rank else 64, rank, seed=M, outliers=(3, K - 5),
+                       zero_rows=(0,) if M > 2 else ())
+    qx, sx, T = H.run_quantize_act(p["X"]["bits"], p["abi"], rank)
+    cx, csx = sq.quantize_activations(p["X"]["values"], p["prep"]["s"])
+    assert np.array_equal(H.host(qx), sq.pack_int4(cx))
+    assert np.array_equal(H.host(sx), csx)
+    if rank:
+        check_T(T, sq.lowrank_down(p["X"]["values"], p["prep"]["L1s"]))
+
+
+def test_quantize_act_attention_projection_full():
+    case, X, W, bias, prep, abi = H.prepared_case("attn_proj")
+    say("quantize_act attn_proj", X["bits"].shape)
+    qx, sx, T = H.run_quantize_act(X["bits"], abi, case.rank)
+    cx, csx = sq.quantize_activations(X["values"], prep["s"])
+    assert np.array_equal(H.host(qx), sq.pack_int4(cx))
+    assert np.array_equal(H.host(sx), csx)
+    check_T(T, sq.lowrank_down(X["values"], prep["L1s"]))
+
+
+def test_channel_absmax_matches_oracle():
+    t = H.torch()
+    say("channel_absmax")
+    case = wl.CASES["attn_proj"]
+    X = wl.activations(case, 1000)
+    am = t.zeros(case.K, dtype=t.float32, device="cuda")
+    b.svdq_channel_absmax(H.dev(X["bits"][:600]), am)
+    b.svdq_channel_absmax(H.dev(X["bits"][600:]), am)  # running max over two batches
+    t.cuda.synchronize()
+    assert np.array_equal(H.host(am), sq.channel_absmax(X["values"]))
+
+
+# ----------------------------------------------------------- partials ---
+
+@pytest.mark.parametrize("shape", [(64, 256, 256), (100, 192, 136), (130, 128, 264)])
+def test_group_partials_bit_exact(shape):
+    M, K, N = shape
+    say("partials", shape)
+    t = H.torch()
+    rng = np.random.default_rng(M + K + N)
+    cx = rng.integers(-7, 8, (M, K)).astype(np.int8)
+    cw = rng.integers(-7, 8, (K, N)).astype(np.int8)
+    cx[0, :64] = 7
+    cw[:64, 0] = 7  # the largest partial, 64 * 49
+    cx[1, :64] = -7
+    P = t.empty((K // 64, M, N), dtype=t.int32, device="cuda")
+    b.svdq_debug_group_partials(H.dev(sq.pack_int4(cx)), H.dev(sq.pack_int4(cw.T)), P, M, N, K)
+    t.cuda.synchronize()
+    ref = sq.group_partials(cx, cw)
+    assert np.array_equal(H.host(P).astype(np.int64), ref)
+    assert ref[0, 0, 0] == 64 * 49 and ref[0, 1, 0] == -64 * 49
+
+
+# -------------------------------------------------------------- linear ---
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_w4a4_linear_tiny(out):
+    case, X, W, bias, prep, abi = H.prepared_case("tiny")
+    say("linear tiny", out)
+    M, K, N, r = case.M, case.K, case.N, case.rank
+    qx, sx, T = H.run_quantize_act(X["bits"], abi, r)
+    Y = H.run_linear(qx, sx, T, abi, bias["bits"], M, N, K, r, out)
+    ref = sq.forward(X["values"], prep, bias["values"], out)
+    check_output(H.y_values(Y, out), ref["y"])
+    # the GEMM alone on the oracle's own codes, scales and T
+    Y2 = H.run_linear(H.dev(sq.pack_int4(ref["qx"])), H.dev(ref["sx"]), H.dev(sq.bf16_bits(ref["T"])),
+                      abi, bias["bits"], M, N, K, r, out)
+    check_output(H.y_values(Y2, out), ref["y"])
+
+
+@pytest.mark.parametrize("shape", [(77, 320, 200, 16), (1, 64, 16, 16), (257, 512, 136, 32), (130, 256, 264, 0),
+                                   (65, 128, 384, 64)])
+def test_w4a4_linear_ragged(shape):
+    M, K, N, r = shape
+    say("linear ragged", shape)
+    p = H.make_problem(M, K, N, r, seed=N, outliers=(1,), zero_rows=(M - 1,) if M > 1 else ())
+    qx, sx, T = H.run_quantize_act(p["X"]["bits"], p["abi"], r)
+    Y = H.run_linear(qx, sx, T, p["abi"], p["bias"]["bits"], M, N, K, r, "f32")
+    ref = sq.forward(p["X"]["values"], p["prep"], p["bias"]["values"], "f32")
+    check_output(H.y_values(Y, "f32"), ref["y"])
+
+
+def test_w4a4_linear_no_bias_zero_rows():
+    M, K, N, r = 40, 128, 64, 16
+    say("linear no bias")
+    p = H.make_problem(M, K, N, r, seed=5, bias=False, zero_rows=(0, 7, 39))
+    qx, sx, T = H.run_quantize_act(p["X"]["bits"], p["abi"], r)
+    Y = H.run_linear(qx, sx, T, p["abi"], None, M, N, K, r, "f32")
+    ref = sq.forward(p["X"]["values"], p["prep"], None, "f32")
+    y = H.y_values(Y, "f32")
+    check_output(y, ref["y"])
+    assert np.all(y[[0, 7, 39]] == 0.0)
+
+
+def test_w4a4_attention_projection_full():
+    case, X, W, bias, prep, abi = H.prepared_case("attn_proj")
+    M, K, N, r = case.M, case.K, case.N, case.rank
+    say("linear attn_proj full", (M, K, N, r))
+    qx, sx, T = H.run_quantize_act(X["bits"], abi, r)
+    Y = H.run_linear(qx, sx, T, abi, bias["bits"], M, N, K, r, "bf16")
+    ref = sq.forward(X["values"], prep, bias["values"], "bf16")
+    check_output(H.y_values(Y, "bf16"), ref["y"])
+    # the quality of the method itself is reported, not gated
+    say("  rel-L2 vs unquantized X W + b:",
+        rel_l2(ref["y64"], X["values"].astype(F64) @ W["values"].astype(F64) + bias["values"]))
+
+
+def _sampled_rows(M, count=96, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(M, size=min(count, M), replace=False).tolist())
+    rows |= {0, 1, M - 1, M - 2, min(M - 1, (M // 128) * 128), min(M - 1, 127), min(M - 1, 128)}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["mlp_up", "video"])
+def test_w4a4_full_size_sampled_rows(name):
+    """Full-size shapes in the launch configuration the bench times; the
+    oracle recomputes sampled token rows (the method is row-local)."""
+    case, X, W, bias, prep, abi = H.prepared_case(name)
+    M, K, N, r = case.M, case.K, case.N, case.rank
+    say("linear full-size", name, (M, K, N, r))
+    qx, sx, T = H.run_quantize_act(X["bits"], abi, r)
+    Y = H.run_linear(qx, sx, T, abi, bias["bits"], M, N, K, r, "bf16")
+    rows = _sampled_rows(M)
+    ref = sq.forward(X["values"][rows], prep, bias["values"], "bf16")
+    cx = ref["qx"]
+    assert np.array_equal(H.host(qx)[rows], sq.pack_int4(cx))
+    assert np.array_equal(H.host(sx)[:, rows], ref["sx"])
+    check_T(H.host(T)[rows], ref["T"])
+    y = sq.bf16_from_bits(H.host(Y).view(np.uint16)[rows])
+    check_output(y, ref["y"])
+
+
+def test_w4a4_mlp_down_projection_sampled():
+    """The MLP pair's second projection: input = GELU of the oracle's
+    up-projection output (on the host), K = 12288."""
+    case, X, W, bias, prep, abi = H.prepared_case("mlp_up")
+    say("linear mlp_down")
+    rows = np.arange(0, 640)  # five full row tiles of 128
+    up = sq.forward(X["values"][rows], prep, bias["values"], "bf16")
+    G = wl.gelu_bf16(up["y"])
+    Wd = wl.mlp_down_weight()
+    bd = wl.mlp_down_bias()
+    a = sq.channel_absmax(G["values"])
+    prep_d = sq.prepare_weights(Wd["values"], a, 32)
+    abi_d = sq.to_abi(prep_d)
+    M, K, N = len(rows), wl.MLP_DOWN.K, wl.MLP_DOWN.N
+    qx, sx, T = H.run_quantize_act(G["bits"], abi_d, 32)
+    Y = H.run_linear(qx, sx, T, abi_d, bd["bits"], M, N, K, 32, "bf16")
+    ref = sq.forward(G["values"], prep_d, bd["values"], "bf16")
+    assert np.array_equal(H.host(qx), sq.pack_int4(ref["qx"]))
+    check_output(H.y_values(Y, "bf16"), ref["y"])
+
+
+# -------------------------------------------------------- metamorphic ---
+
+def test_power_of_two_scaling_and_negation_are_exact():
+    M, K, N, r = 96, 256, 128, 16
+    say("metamorphic")
+    p = H.make_problem(M, K, N, r, seed=3, bias=False)
+    Xv = p["X"]["values"].astype(np.float32)
+    outs = {}
+    for tag, f in (("x1", 1.0), ("x4", 4.0), ("neg", -1.0)):
+        bits = wl.bf16_bits_from_f32(Xv * np.float32(f))
+        qx, sx, T = H.run_quantize_act(bits, p["abi"], r)
+        Y = H.run_linear(qx, sx, T, p["abi"], None, M, N, K, r, "f32")
+        outs[tag] = (H.host(qx), H.host(sx), H.host(T), H.y_values(Y, "f32"))
+    cx1 = sq.unpack_int4(outs["x1"][0])
+    assert np.array_equal(outs["x4"][0], outs["x1"][0])
+    assert np.array_equal(outs["x4"][1], outs["x1"][1] * 4)
+    assert np.array_equal(outs["x4"][3], outs["x1"][3] * 4)
+    assert np.array_equal(sq.unpack_int4(outs["neg"][0]), -cx1)
+    assert np.array_equal(outs["neg"][3], -outs["x1"][3])
+
+
+def test_run_to_run_byte_identical():
+    case, X, W, bias, prep, abi = H.prepared_case("tiny")
+    say("determinism")
+    M, K, N, r = case.M, case.K, case.N, case.rank
+    res = []
+    for _ in range(3):
+        qx, sx, T = H.run_quantize_act(X["bits"], abi, r)
+        Y = H.run_linear(qx, sx, T, abi, bias["bits"], M, N, K, r, "bf16")
+        res.append((H.host(qx).tobytes(), H.host(sx).tobytes(), H.host(T).tobytes(), H.host(Y).tobytes()))
+    assert res[0] == res[1] == res[2]
+
+
+def test_empty_batch_is_a_no_op():
+    t = H.torch()
+    say("M = 0")
+    K, N, r = 128, 64, 16
+    p = H.make_problem(8, K, N, r, seed=9)
+    e16 = t.empty((0, K), dtype=t.int16, device="cuda")
+    qx = t.empty((0, K // 2), dtype=t.uint8, device="cuda")
+    sx = t.empty((K // 64, 0), dtype=t.float32, device="cuda")
+    T = t.empty((0, r), dtype=t.int16, device="cuda")
+    b.svdq_quantize_act(e16, H.dev(p["abi"]["s"]), H.dev(p["abi"]["l1t"]), qx, sx, T, r)
+    Y = t.empty((0, N), dtype=t.int16, device="cuda")
+    b.svdq_w4a4_linear(qx, sx, T, H.dev(p["abi"]["qw"]), H.dev(p["abi"]["sw"]), H.dev(p["abi"]["l2t"]),
+                       None, Y, 0, N, K, r)
+    t.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- W8A8 ---
+
+@pytest.mark.parametrize("shape", [(64, 256, 256), (77, 192, 136), (1, 64, 8)])
+def test_w8a8_small(shape):
+    M, K, N = shape
+    say("w8a8", shape)
+    X = wl.random_bf16(M * 7 + K, (M, K))
+    Xv = X["values"].copy()
+    Xv[:, 2] *= 10
+    Xb = wl.bf16_bits_from_f32(Xv)
+    Xv = wl.f32_from_bf16_bits(Xb)
+    W = wl.random_bf16(N + 1, (K, N), 0.02)
+    bias = wl.random_bf16(N + 2, (N,), 0.01)
+    qw, sw = o8.prepare_weights(W["values"])
+    Y, codes, scale = H.w8a8_run(Xb, o8.to_abi(qw), float(sw), bias["bits"])
+    ref = o8.forward(Xv, qw, sw, bias["values"])
+    assert scale == float(ref["sx"])
+    assert np.array_equal(codes, ref["qx"])
+    check_output(H.y_values(Y, "bf16"), ref["y"])
+
+
+def test_w8a8_attention_shape_full():
+    case = wl.CASES["w8a8_attn"]
+    say("w8a8 full", (case.M, case.K, case.N))
+    X = wl.activations(case)
+    W = wl.weight(case)
+    bias = wl.bias(case)
+    qw, sw = o8.prepare_weights(W["values"])
+    Y, codes, scale = H.w8a8_run(X["bits"], o8.to_abi(qw), float(sw), bias["bits"])
+    ref = o8.forward(X["values"], qw, sw, bias["values"])
+    assert scale == float(ref["sx"])
+    assert np.array_equal(codes, ref["qx"])
+    check_output(H.y_values(Y, "bf16"), ref["y"])
+
+
+@pytest.mark.parametrize("shape", [(64, 256, 256), (130, 320, 136)])
+def test_w8a8_accumulators_bit_exact(shape):
+    M, K, N = shape
+    say("w8a8 acc", shape)
+    t = H.torch()
+    rng = np.random.default_rng(K)
+    qx = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    qw = rng.integers(-127, 128, (K, N)).astype(np.int8)
+    qx[0, :] = 127
+    qw[:, 0] = 127
+    acc = t.empty((M, N), dtype=t.int32, device="cuda")
+    b.w8a8_debug_acc(H.dev(qx), H.dev(o8.to_abi(qw)), acc, M, N, K)
+    t.cuda.synchronize()
+    ref = o8.accumulate(qx, qw)
+    assert np.array_equal(H.host(acc).astype(np.int64), ref)
+    assert ref[0, 0] == K * 127 * 127
