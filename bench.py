@@ -5,15 +5,19 @@
 
 One step is one pass of the linear's device path over one batch: the fused
 activation quantization (svdq_quantize_act: smoothing divide, group absmax,
-INT4 packing, low-rank down-projection) followed by the W4A4 GEMM with its
-fused low-rank up-projection and bias (svdq_w4a4_linear). Weights are
-prepared once beforehand by the library's host preparation and stay resident
-in HBM; inputs are resident before the timed region starts.
+INT4 codes, low-rank down-projection) followed by the W4A4 GEMM with its
+fused low-rank up-projection and bias (svdq_w4a4_linear). The codes travel in
+the FP6 container (gfx950's FP6 MFMA); the same step on the compact INT4
+container (i8 MFMA) is timed beside it. Weights are prepared once beforehand
+by the library's host preparation (and re-encoded by svdq_repack_codes) and
+stay resident in HBM; inputs are resident before the timed region starts.
 
-Prints ONE JSON line. `value` is TOPS counted as 2 M N K integer operations
-per step over the whole step (both kernels); the roofline object describes the
-dominant kernel (the GEMM) against the int8 MFMA peak. The W8A8 linear on the
-attention shape is timed the same way and reported under "w8a8".
+Prints ONE JSON line. `value` is TOPS counted as 2 M N K operations per step
+over the whole step (both kernels). The roofline object describes the
+dominant kernel (the GEMM) against the dense peak of the MFMA type it runs on
+(FP6); "pct_int8_roofline" gives the same throughput against the int8 MFMA
+peak. The W8A8 linear on the attention shape is timed the same way and
+reported under "w8a8".
 """
 
 from __future__ import annotations
@@ -30,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published
+FP6_PEAK_TFLOPS = 10100.0  # MI355X dense FP6/FP4 MFMA, published
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
 
 METRIC = "W4A4+lowrank linear TOPS & % int8 MFMA roofline at M=4608,K=3072,N=12288"
@@ -43,7 +48,7 @@ def parse():
     p.add_argument("--workload", default="mlp_up")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-w8a8", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=384,
+    p.add_argument("--cpu-rows", type=int, default=4608,
                    help="token rows of the workload the CPU oracle is timed on")
     return p.parse_args()
 
@@ -159,22 +164,32 @@ def main():
 
     s_d, l1_d, l2_d = up(prep["s"]), up(prep["l1t"]), up(prep["l2t"])
     qw_d, sw_d, b_d = up(prep["qw"]), up(prep["sw"]), up(bias["bits"])
+    qw6_d = up(b.svdq_repack_codes(prep["qw"], K, b.QFMT_FP6))
     qx = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+    qx6 = torch.empty((M, b.svdq_qrow_bytes(K, b.QFMT_FP6)), dtype=torch.uint8, device="cuda")
     sx = torch.empty((K // 64, M), dtype=torch.float32, device="cuda")
     T = torch.empty((M, r), dtype=torch.int16, device="cuda")
     Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
 
-    def act():
-        b.svdq_quantize_act(Xd, s_d, l1_d, qx, sx, T, r)
+    def act6():
+        b.svdq_quantize_act(Xd, s_d, l1_d, qx6, sx, T, r, qfmt=b.QFMT_FP6)
 
-    def gemm():
-        b.svdq_w4a4_linear(qx, sx, T, qw_d, sw_d, l2_d, b_d, Y, M, N, K, r)
+    def gemm6():
+        b.svdq_w4a4_linear(qx6, sx, T, qw6_d, sw_d, l2_d, b_d, Y, M, N, K, r, qfmt=b.QFMT_FP6)
 
-    ms, per, wall = time_steps([act, gemm], args.steps, args.warmup)
+    def act4():
+        b.svdq_quantize_act(Xd, s_d, l1_d, qx, sx, T, r, qfmt=b.QFMT_INT4)
+
+    def gemm4():
+        b.svdq_w4a4_linear(qx, sx, T, qw_d, sw_d, l2_d, b_d, Y, M, N, K, r, qfmt=b.QFMT_INT4)
+
+    ms4, per4, _ = time_steps([act4, gemm4], args.steps, args.warmup)
+    log(f"[bench] int4 container: step {ms4:.4f} ms (act {per4[0]:.4f} ms, gemm {per4[1]:.4f} ms)")
+    ms, per, wall = time_steps([act6, gemm6], args.steps, args.warmup)
     ops = 2.0 * M * N * K
     tops = ops / (ms * 1e-3) / 1e12
     gemm_tops = ops / (per[1] * 1e-3) / 1e12
-    act_bytes = M * K * 2 + r * K * 2 + K * 4 + M * K // 2 + (K // 64) * M * 4 + M * r * 2
+    act_bytes = M * K * 2 + r * K * 2 + K * 4 + M * (K // 4 * 3) + (K // 64) * M * 4 + M * r * 2
     act_gbs = act_bytes / (per[0] * 1e-3) / 1e9
     y_finite = bool(torch.isfinite(Y.view(torch.bfloat16).float()).all().item())
     log(f"[bench] step {ms:.4f} ms (act {per[0]:.4f} ms, gemm {per[1]:.4f} ms) -> {tops:.1f} TOPS")
@@ -190,7 +205,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 x int4 (i8 MFMA) + bf16 low-rank, bf16 out",
+        "dtype": "int4 codes x int4 codes (FP6 MFMA, exact) + fp32 scales + bf16 low-rank, bf16 out",
         "data": "synthetic (seeded N(0,1) activations with outlier channels, N(0,0.02) weights "
                 "with heavy columns, random init; no checkpoint)",
         "config": {"workload": f"{case.name}: SVDQuant W4A4 linear M={M} K={K} N={N} rank={r} group=64",
@@ -203,9 +218,13 @@ def main():
             "svdq_w4a4_linear": {"ms": round(per[1], 5), "TOPS": round(gemm_tops, 2),
                                  "pct_int8_roofline": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2)},
         },
-        "roofline": {"bound": "mfma", "kernel": "svdq_w4a4_linear",
-                     "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": None},
+        "int4_container": {"ms_per_step": round(ms4, 5), "TOPS": round(ops / (ms4 * 1e-3) / 1e12, 2),
+                           "act_ms": round(per4[0], 5), "gemm_ms": round(per4[1], 5),
+                           "gemm_TOPS": round(ops / (per4[1] * 1e-3) / 1e12, 2),
+                           "gemm_pct_int8_roofline": round(100.0 * ops / (per4[1] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)},
+        "roofline": {"bound": "mfma", "kernel": "svdq_w4a4_linear (FP6 container)", "mfma_dtype": "fp6",
+                     "achieved": round(gemm_tops, 2), "peak": FP6_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tops / FP6_PEAK_TFLOPS, 4), "traffic": None},
         "wall_ms_per_step": round(wall, 5),
         "outputs_finite": y_finite,
     }

@@ -25,6 +25,8 @@ SVDQ_ERR_NUMERICAL = 5
 SVDQ_ERR_HIP = 6
 SVDQ_BF16 = 0
 SVDQ_F32 = 1
+QFMT_INT4 = 0
+QFMT_FP6 = 1
 GROUP = 64
 
 _vp, _i, _f, _sz = C.c_void_p, C.c_int, C.c_float, C.c_size_t
@@ -33,16 +35,18 @@ _vp, _i, _f, _sz = C.c_void_p, C.c_int, C.c_float, C.c_size_t
 SIGNATURES = {
     "svdq_status_string": (C.c_char_p, [_i]),
     "svdq_version": (_i, []),
+    "svdq_qrow_bytes": (_sz, [_i, _i]),
+    "svdq_repack_codes": (_i, [_vp, _i, _i, _i, _vp]),
     "svdq_check_device": (_i, [_i]),
     "svdq_prepare_weights": (_i, [_vp, _i, _i, _vp, _f, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "svdq_prepare_residual": (_i, [_vp, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp]),
     "w8a8_prepare_weights": (_i, [_vp, _i, _i, _vp, _vp]),
     "svdq_channel_absmax": (_i, [_vp, _i, _i, _vp, _vp]),
-    "svdq_quantize_act": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
-    "svdq_w4a4_linear": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp]),
+    "svdq_quantize_act": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "svdq_w4a4_linear": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
     "w8a8_workspace_bytes": (_sz, [_i, _i]),
     "w8a8_linear": (_i, [_vp, _vp, _f, _vp, _i, _i, _i, _vp, _sz, _vp, _vp]),
-    "svdq_debug_group_partials": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "svdq_debug_group_partials": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "w8a8_debug_acc": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
     "svdq_debug_set_arch_override": (_i, [C.c_char_p]),
 }
@@ -116,6 +120,10 @@ def svdq_version() -> int:
     return lib().svdq_version()
 
 
+def svdq_qrow_bytes(K: int, qfmt: int) -> int:
+    return int(lib().svdq_qrow_bytes(K, qfmt))
+
+
 def svdq_check_device(device: int = 0) -> int:
     return lib().svdq_check_device(device)
 
@@ -166,6 +174,17 @@ def svdq_prepare_residual(W_bits, smooth, l1t, l2t, group=GROUP):
     return {"qw": qw, "sw": sw}
 
 
+def svdq_repack_codes(q, K, qfmt):
+    """Canonical INT4 rows [rows, K/2] -> container `qfmt` rows."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    rows = q.shape[0]
+    out = np.empty((rows, svdq_qrow_bytes(K, qfmt)), np.uint8)
+    st = lib().svdq_repack_codes(q.ctypes.data if rows else None, rows, K, qfmt,
+                                 out.ctypes.data if rows else None)
+    _check("svdq_repack_codes", st)
+    return out
+
+
 def w8a8_prepare_weights(W_bits):
     W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
     K, N = W_bits.shape
@@ -184,18 +203,20 @@ def svdq_channel_absmax(X, absmax, stream=None):
     _check("svdq_channel_absmax", st)
 
 
-def svdq_quantize_act(X, smooth, l1t, qx, sx, T, rank, group=GROUP, stream=None):
+def svdq_quantize_act(X, smooth, l1t, qx, sx, T, rank, group=GROUP, qfmt=QFMT_INT4, stream=None):
     M, K = X.shape
     st = lib().svdq_quantize_act(_dev_ptr(X, 2), _dev_ptr(smooth, 4), _dev_ptr(l1t, 2), M, K, rank,
-                                 group, _dev_ptr(qx, 1), _dev_ptr(sx, 4), _dev_ptr(T, 2), _stream(stream))
+                                 group, qfmt, _dev_ptr(qx, 1), _dev_ptr(sx, 4), _dev_ptr(T, 2),
+                                 _stream(stream))
     _check("svdq_quantize_act", st)
 
 
-def svdq_w4a4_linear(qx, sx, T, qw, sw, l2t, bias, Y, M, N, K, rank, group=GROUP, stream=None):
+def svdq_w4a4_linear(qx, sx, T, qw, sw, l2t, bias, Y, M, N, K, rank, group=GROUP, qfmt=QFMT_INT4,
+                     stream=None):
     y_dtype = SVDQ_F32 if Y.element_size() == 4 else SVDQ_BF16
     st = lib().svdq_w4a4_linear(_dev_ptr(qx, 1), _dev_ptr(sx, 4), _dev_ptr(T, 2), _dev_ptr(qw, 1),
                                 _dev_ptr(sw, 4), _dev_ptr(l2t, 2), _dev_ptr(bias, 2), M, N, K, rank,
-                                group, _dev_ptr(Y), y_dtype, _stream(stream))
+                                group, qfmt, _dev_ptr(Y), y_dtype, _stream(stream))
     _check("svdq_w4a4_linear", st)
 
 
@@ -212,8 +233,8 @@ def w8a8_linear(X, qw, sw, bias, workspace, Y, stream=None):
     _check("w8a8_linear", st)
 
 
-def svdq_debug_group_partials(qx, qw, P, M, N, K, group=GROUP, stream=None):
-    st = lib().svdq_debug_group_partials(_dev_ptr(qx, 1), _dev_ptr(qw, 1), M, N, K, group,
+def svdq_debug_group_partials(qx, qw, P, M, N, K, group=GROUP, qfmt=QFMT_INT4, stream=None):
+    st = lib().svdq_debug_group_partials(_dev_ptr(qx, 1), _dev_ptr(qw, 1), M, N, K, group, qfmt,
                                          _dev_ptr(P, 4), _stream(stream))
     _check("svdq_debug_group_partials", st)
 

@@ -27,6 +27,7 @@ constexpr int kActRows = 16;   // token rows per block (one 16x16 MFMA row tile)
 // rank tile (8 channels each); B comes from l1t with the same channel
 // mapping. The 8 waves' fp32 partial T tiles are summed in wave order through
 // LDS, so T is deterministic.
+template <bool kFp6>
 __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ smooth,
     const uint16_t *__restrict__ l1t, int M, int K, int rank,
@@ -75,20 +76,45 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
         amax = fmaxf(amax, __shfl_xor(amax, 32));
         const float scale = amax / 7.0f;
 
-        uint32_t packed[2] = {0u, 0u};
-        if (scale != 0.0f) {
+        if constexpr (!kFp6) {
+            // INT4 container: two's-complement nibbles, low nibble = even k
+            uint32_t packed[2] = {0u, 0u};
+            if (scale != 0.0f) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float q = rintf(xh[t] / scale);  // round half to even
-                q = fminf(7.0f, fmaxf(-7.0f, q));
-                const uint32_t nib = (uint32_t)((int)q) & 0xFu;
-                packed[t >> 3] |= nib << (4 * (t & 7));
+                for (int t = 0; t < 16; ++t) {
+                    float q = rintf(xh[t] / scale);  // round half to even
+                    q = fminf(7.0f, fmaxf(-7.0f, q));
+                    const uint32_t nib = (uint32_t)((int)q) & 0xFu;
+                    packed[t >> 3] |= nib << (4 * (t & 7));
+                }
+            }
+            if (row_ok)
+                *reinterpret_cast<u32x2 *>(qx + (size_t)m * (K / 2) + kb / 2) = u32x2{packed[0], packed[1]};
+        } else {
+            // FP6 container: each code c as FP6 E2M3 of value c / 8 (sign bit,
+            // zero exponent, 3-bit magnitude), 6-bit fields packed LSB-first;
+            // the lane's 16 codes fill bytes [12 quad, +12) of the group's 48
+            uint32_t w[3] = {0u, 0u, 0u};
+            if (scale != 0.0f) {
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    float q = rintf(xh[t] / scale);  // round half to even
+                    q = fminf(7.0f, fmaxf(-7.0f, q));
+                    const int qi = (int)q;
+                    const uint32_t v = (qi < 0 ? 0x20u : 0u) | (uint32_t)(qi < 0 ? -qi : qi);
+                    const int bit = 6 * t;
+                    w[bit >> 5] |= v << (bit & 31);
+                    if ((bit & 31) > 26) w[(bit >> 5) + 1] |= v >> (32 - (bit & 31));
+                }
+            }
+            if (row_ok) {
+                uint32_t *dst = reinterpret_cast<uint32_t *>(qx + (size_t)m * (K / 4 * 3) + (size_t)g * 48 + 12 * quad);
+                dst[0] = w[0];
+                dst[1] = w[1];
+                dst[2] = w[2];
             }
         }
-        if (row_ok) {
-            *reinterpret_cast<u32x2 *>(qx + (size_t)m * (K / 2) + kb / 2) = u32x2{packed[0], packed[1]};
-            if (quad == 0) sx[(size_t)g * M + m] = scale;
-        }
+        if (row_ok && quad == 0) sx[(size_t)g * M + m] = scale;
 
         // low-rank down-projection on raw X (1/s folded into L1s)
 #pragma unroll
@@ -167,11 +193,15 @@ __global__ __launch_bounds__(256) void channel_absmax_kernel(const uint16_t *__r
 }  // namespace
 
 hipError_t launch_quantize_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M,
-                               int K, int rank, uint8_t *qx, float *sx, uint16_t *T,
+                               int K, int rank, int qfmt, uint8_t *qx, float *sx, uint16_t *T,
                                hipStream_t stream) {
     const dim3 grid((M + kActRows - 1) / kActRows);
-    hipLaunchKernelGGL(quantize_act_kernel, grid, dim3(kActWaves * 64), 0, stream, X, smooth, l1t, M,
-                       K, rank, qx, sx, T);
+    if (qfmt == SVDQ_QFMT_FP6)
+        hipLaunchKernelGGL(quantize_act_kernel<true>, grid, dim3(kActWaves * 64), 0, stream, X, smooth, l1t,
+                           M, K, rank, qx, sx, T);
+    else
+        hipLaunchKernelGGL(quantize_act_kernel<false>, grid, dim3(kActWaves * 64), 0, stream, X, smooth, l1t,
+                           M, K, rank, qx, sx, T);
     return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kMaxDevices = 64;
 
 std::mutex g_mutex;
@@ -99,6 +99,13 @@ const char *svdq_status_string(int status) {
 
 int svdq_version(void) { return kAbiVersion; }
 
+size_t svdq_qrow_bytes(int K, int qfmt) {
+    if (K <= 0 || K % SVDQ_GROUP) return 0;
+    if (qfmt == SVDQ_QFMT_INT4) return (size_t)K / 2;
+    if (qfmt == SVDQ_QFMT_FP6) return (size_t)K / 4 * 3;
+    return 0;
+}
+
 svdq_status svdq_check_device(int device) { return device_ok(device); }
 
 svdq_status svdq_debug_set_arch_override(const char *arch) {
@@ -150,6 +157,14 @@ svdq_status svdq_prepare_residual(const uint16_t *W, int K, int N,
     return svdq::prepare_residual_impl(W, K, N, smooth, l1t, l2t, rank, qw, sw);
 }
 
+svdq_status svdq_repack_codes(const uint8_t *q, int rows, int K, int qfmt, uint8_t *out) {
+    if (rows < 0 || K <= 0) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (qfmt != SVDQ_QFMT_INT4 && qfmt != SVDQ_QFMT_FP6) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (K % SVDQ_GROUP) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    if (rows > 0 && (!q || !out)) return SVDQ_ERR_INVALID_ARGUMENT;
+    return svdq::repack_codes_impl(q, rows, K, qfmt, out);
+}
+
 svdq_status w8a8_prepare_weights(const uint16_t *W, int K, int N, int8_t *qw, float *sw) {
     if (!W || !qw || !sw || K <= 0 || N <= 0) return SVDQ_ERR_INVALID_ARGUMENT;
     if (!svdq::all_finite_bf16(W, (int64_t)K * N)) return SVDQ_ERR_NUMERICAL;
@@ -171,10 +186,11 @@ svdq_status svdq_channel_absmax(const uint16_t *X, int M, int K, float *absmax, 
 
 svdq_status svdq_quantize_act(const uint16_t *X, const float *smooth,
                               const uint16_t *l1t, int M, int K, int rank,
-                              int group, uint8_t *qx, float *sx, uint16_t *T,
-                              void *stream) {
+                              int group, int qfmt, uint8_t *qx, float *sx,
+                              uint16_t *T, void *stream) {
     svdq_status st = check_w4a4_shape(M, K, rank, group);
     if (st != SVDQ_OK) return st;
+    if (qfmt != SVDQ_QFMT_INT4 && qfmt != SVDQ_QFMT_FP6) return SVDQ_ERR_INVALID_ARGUMENT;
     if (!smooth || (M > 0 && (!X || !qx || !sx))) return SVDQ_ERR_INVALID_ARGUMENT;
     if (rank > 0 && (!l1t || (M > 0 && !T))) return SVDQ_ERR_INVALID_ARGUMENT;
     if (!aligned16(X) || !aligned16(smooth) || !aligned16(l1t) || !aligned16(qx) ||
@@ -183,7 +199,7 @@ svdq_status svdq_quantize_act(const uint16_t *X, const float *smooth,
     st = current_device_ok();
     if (st != SVDQ_OK) return st;
     if (M == 0) return SVDQ_OK;
-    return launched(svdq::launch_quantize_act(X, smooth, rank ? l1t : nullptr, M, K, rank, qx, sx,
+    return launched(svdq::launch_quantize_act(X, smooth, rank ? l1t : nullptr, M, K, rank, qfmt, qx, sx,
                                               rank ? T : nullptr, (hipStream_t)stream));
 }
 
@@ -191,10 +207,11 @@ svdq_status svdq_w4a4_linear(const uint8_t *qx, const float *sx,
                              const uint16_t *T, const uint8_t *qw,
                              const float *sw, const uint16_t *l2t,
                              const uint16_t *bias, int M, int N, int K,
-                             int rank, int group, void *Y, int y_dtype,
-                             void *stream) {
+                             int rank, int group, int qfmt, void *Y,
+                             int y_dtype, void *stream) {
     svdq_status st = check_w4a4_shape(M, K, rank, group);
     if (st != SVDQ_OK) return st;
+    if (qfmt != SVDQ_QFMT_INT4 && qfmt != SVDQ_QFMT_FP6) return SVDQ_ERR_INVALID_ARGUMENT;
     if (N <= 0) return SVDQ_ERR_INVALID_ARGUMENT;
     if (N % 8) return SVDQ_ERR_UNSUPPORTED_SHAPE;
     if (y_dtype != SVDQ_BF16 && y_dtype != SVDQ_F32) return SVDQ_ERR_INVALID_ARGUMENT;
@@ -206,6 +223,10 @@ svdq_status svdq_w4a4_linear(const uint8_t *qx, const float *sx,
     st = current_device_ok();
     if (st != SVDQ_OK) return st;
     if (M == 0) return SVDQ_OK;
+    if (qfmt == SVDQ_QFMT_FP6)
+        return launched(svdq::launch_w4a4_fp6_linear(qx, sx, rank ? T : nullptr, qw, sw,
+                                                     rank ? l2t : nullptr, bias, M, N, K, rank, Y,
+                                                     y_dtype == SVDQ_F32, (hipStream_t)stream));
     return launched(svdq::launch_w4a4_linear(qx, sx, rank ? T : nullptr, qw, sw, rank ? l2t : nullptr,
                                              bias, M, N, K, rank, Y, y_dtype == SVDQ_F32,
                                              (hipStream_t)stream));
@@ -235,10 +256,11 @@ svdq_status w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
 }
 
 svdq_status svdq_debug_group_partials(const uint8_t *qx, const uint8_t *qw,
-                                      int M, int N, int K, int group,
+                                      int M, int N, int K, int group, int qfmt,
                                       int32_t *P, void *stream) {
     svdq_status st = check_w4a4_shape(M, K, 0, group);
     if (st != SVDQ_OK) return st;
+    if (qfmt != SVDQ_QFMT_INT4 && qfmt != SVDQ_QFMT_FP6) return SVDQ_ERR_INVALID_ARGUMENT;
     if (N <= 0) return SVDQ_ERR_INVALID_ARGUMENT;
     if (N % 8) return SVDQ_ERR_UNSUPPORTED_SHAPE;
     if (!qw || (M > 0 && (!qx || !P))) return SVDQ_ERR_INVALID_ARGUMENT;
@@ -246,6 +268,8 @@ svdq_status svdq_debug_group_partials(const uint8_t *qx, const uint8_t *qw,
     st = current_device_ok();
     if (st != SVDQ_OK) return st;
     if (M == 0) return SVDQ_OK;
+    if (qfmt == SVDQ_QFMT_FP6)
+        return launched(svdq::launch_w4a4_fp6_partials(qx, qw, M, N, K, P, (hipStream_t)stream));
     return launched(svdq::launch_w4a4_partials(qx, qw, M, N, K, P, (hipStream_t)stream));
 }
 

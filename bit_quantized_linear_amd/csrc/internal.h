@@ -20,6 +20,7 @@ svdq_status prepare_residual_impl(const uint16_t *W, int K, int N,
                                   const uint16_t *l2t, int rank, uint8_t *qw,
                                   float *sw);
 svdq_status w8a8_prepare_impl(const uint16_t *W, int K, int N, int8_t *qw, float *sw);
+svdq_status repack_codes_impl(const uint8_t *q, int rows, int K, int qfmt, uint8_t *out);
 svdq_status truncated_svd(const double *A, int K, int N, int rank, double *U,
                           double *S, double *V);
 bool all_finite_bf16(const uint16_t *p, int64_t n);
@@ -30,7 +31,7 @@ hipError_t launch_channel_absmax(const uint16_t *X, int M, int K, float *absmax,
                                  hipStream_t stream);
 hipError_t launch_quantize_act(const uint16_t *X, const float *smooth,
                                const uint16_t *l1t, int M, int K, int rank,
-                               uint8_t *qx, float *sx, uint16_t *T,
+                               int qfmt, uint8_t *qx, float *sx, uint16_t *T,
                                hipStream_t stream);
 hipError_t launch_w4a4_linear(const uint8_t *qx, const float *sx,
                               const uint16_t *T, const uint8_t *qw,
@@ -39,6 +40,13 @@ hipError_t launch_w4a4_linear(const uint8_t *qx, const float *sx,
                               int rank, void *Y, bool y_f32, hipStream_t stream);
 hipError_t launch_w4a4_partials(const uint8_t *qx, const uint8_t *qw, int M,
                                 int N, int K, int32_t *P, hipStream_t stream);
+hipError_t launch_w4a4_fp6_linear(const uint8_t *qx, const float *sx,
+                                  const uint16_t *T, const uint8_t *qw,
+                                  const float *sw, const uint16_t *l2t,
+                                  const uint16_t *bias, int M, int N, int K,
+                                  int rank, void *Y, bool y_f32, hipStream_t stream);
+hipError_t launch_w4a4_fp6_partials(const uint8_t *qx, const uint8_t *qw, int M,
+                                    int N, int K, int32_t *P, hipStream_t stream);
 hipError_t launch_w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
                               const uint16_t *bias, int M, int N, int K,
                               void *workspace, uint16_t *Y, hipStream_t stream);

@@ -409,6 +409,37 @@ svdq_status w8a8_prepare_impl(const uint16_t *W, int K, int N, int8_t *qw, float
     return SVDQ_OK;
 }
 
+// Canonical INT4 nibbles -> FP6 E2M3 container (code / 8: sign in bit 5,
+// |code| in bits 0-2), 64 codes per 48 bytes, 6-bit fields LSB-first.
+svdq_status repack_codes_impl(const uint8_t *q, int rows, int K, int qfmt, uint8_t *out) {
+    const int64_t in_row = K / 2;
+    if (qfmt == SVDQ_QFMT_INT4) {
+        std::memcpy(out, q, (size_t)rows * in_row);
+        return SVDQ_OK;
+    }
+    const int64_t out_row = (int64_t)K / 4 * 3;
+    bool bad = false;
+    for (int r = 0; r < rows; ++r) {
+        const uint8_t *src = q + r * in_row;
+        uint8_t *dst = out + r * out_row;
+        for (int g = 0; g < K / 64; ++g) {
+            uint64_t bits[6] = {0, 0, 0, 0, 0, 0};  // 384 bits
+            for (int k = 0; k < 64; ++k) {
+                const uint8_t byte = src[g * 32 + k / 2];
+                const int nib = (k & 1) ? (byte >> 4) : (byte & 0xF);
+                const int code = nib >= 8 ? nib - 16 : nib;
+                if (code == -8) bad = true;
+                const uint64_t v = (code < 0 ? 0x20u : 0u) | (uint64_t)(code < 0 ? -code : code);
+                const int bit = 6 * k;
+                bits[bit / 64] |= v << (bit % 64);
+                if (bit % 64 > 58) bits[bit / 64 + 1] |= v >> (64 - bit % 64);
+            }
+            for (int b = 0; b < 48; ++b) dst[g * 48 + b] = (uint8_t)(bits[b / 8] >> (8 * (b % 8)));
+        }
+    }
+    return bad ? SVDQ_ERR_NUMERICAL : SVDQ_OK;
+}
+
 bool all_finite_bf16(const uint16_t *p, int64_t n) {
     for (int64_t i = 0; i < n; ++i)
         if (!bf16_is_finite(p[i])) return false;

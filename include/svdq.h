@@ -46,10 +46,9 @@
  *  - Calls on different streams may run concurrently; the library keeps no
  *    mutable state apart from a per-device architecture cache.
  *
- * Packed INT4 layout (used by qx and qw): two's-complement nibbles, byte j of
- * a row holds element k = 2j in its low nibble and k = 2j + 1 in its high
- * nibble. Codes lie in [-7, 7] (symmetric grid; -8 never produced).
- * Group scales are fp32, group size G = 64 along K, stored group-major.
+ * Codes lie in [-7, 7] (symmetric grid; -8 never produced); qx and qw hold
+ * them in one of two containers (svdq_qformat below). Group scales are fp32,
+ * group size G = 64 along K, stored group-major.
  */
 #ifndef SVDQ_H
 #define SVDQ_H
@@ -76,6 +75,23 @@ typedef enum svdq_dtype {
     SVDQ_F32 = 1
 } svdq_dtype;
 
+/* Containers for the INT4 codes (values -7..7) of qx and qw. Both hold the
+ * same codes; they differ only in bit layout.
+ *  SVDQ_QFMT_INT4: K/2 bytes per row; two's-complement nibbles, byte j holds
+ *      k = 2j (low nibble) and k = 2j + 1 (high nibble). The compact,
+ *      canonical layout; its GEMM unpacks nibbles to int8 for i8 MFMA.
+ *  SVDQ_QFMT_FP6: 3K/4 bytes per row; per group g of 64 codes, bytes
+ *      [48 g, 48 g + 48) hold code k of the group in bits [6 k, 6 k + 6)
+ *      (little-endian, least significant bit first) as an FP6 E2M3 number
+ *      equal to code / 8: bit 5 = sign, bits 0-2 = |code|, exponent field 0.
+ *      Every INT4 code is exact in this form and gfx950's FP6 MFMA, which
+ *      runs at twice the int8 rate, returns each group's partial sum as an
+ *      exact fp32 integer. */
+typedef enum svdq_qformat {
+    SVDQ_QFMT_INT4 = 0,
+    SVDQ_QFMT_FP6 = 1
+} svdq_qformat;
+
 #define SVDQ_GROUP 64
 #define SVDQ_MAX_RANK 64
 
@@ -84,6 +100,10 @@ const char *svdq_status_string(int status);
 
 /* Library ABI version (bumped on any signature or layout change). */
 int svdq_version(void);
+
+/* Bytes per row of packed codes for K codes in container `qfmt` (0 on a bad
+ * argument): K/2 for SVDQ_QFMT_INT4, 3K/4 for SVDQ_QFMT_FP6. */
+size_t svdq_qrow_bytes(int K, int qfmt);
 
 /* Fail-closed capability check [HF-SVDQ, hardware paragraph]: SVDQ_OK when
  * `device` exists and is gfx950, SVDQ_ERR_UNSUPPORTED_DEVICE otherwise. */
@@ -140,6 +160,13 @@ svdq_status svdq_prepare_residual(const uint16_t *W, int K, int N,
 svdq_status w8a8_prepare_weights(const uint16_t *W, int K, int N,
                                  int8_t *qw, float *sw);
 
+/* Re-encodes packed codes from the canonical INT4 container into `qfmt`
+ * (SVDQ_QFMT_INT4 copies). In: q [rows, K/2]; out: [rows, svdq_qrow_bytes(K,
+ * qfmt)]. Host pointers. Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE (K % 64),
+ * NUMERICAL (a nibble holding -8, which no SVDQuant code uses). */
+svdq_status svdq_repack_codes(const uint8_t *q, int rows, int K, int qfmt,
+                              uint8_t *out);
+
 /* -------------------------------------------------------------- DEVICE --- */
 
 /* Calibration statistic for smoothing (self-calibration: the statistic comes
@@ -160,8 +187,9 @@ svdq_status svdq_channel_absmax(const uint16_t *X, int M, int K, float *absmax,
  *   A == 0 -> sx = 0, codes 0;
  *   T[m, :] = bf16(X[m, :] L1s)  -- the low-rank down-projection on raw X with
  *   1/s folded into L1s, fp32 accumulation, one rounding to bf16.
- * In:  X [M, K] bf16; smooth [K] fp32; l1t [rank, K] bf16 (NULL if rank 0).
- * Out: qx [M, K/2] packed INT4; sx [K/64, M] fp32; T [M, rank] bf16 (NULL if
+ * In:  X [M, K] bf16; smooth [K] fp32; l1t [rank, K] bf16 (NULL if rank 0);
+ *      qfmt: the container of qx (svdq_qformat).
+ * Out: qx [M, svdq_qrow_bytes(K, qfmt)]; sx [K/64, M] fp32; T [M, rank] bf16 (NULL if
  *      rank 0). M >= 0 (M == 0 launches nothing), K % 64 == 0,
  *      rank % 16 == 0, rank <= 64, group == 64.
  * Deterministic: T's partial sums are combined in a fixed order.
@@ -169,18 +197,22 @@ svdq_status svdq_channel_absmax(const uint16_t *X, int M, int K, float *absmax,
  *      HIP. */
 svdq_status svdq_quantize_act(const uint16_t *X, const float *smooth,
                               const uint16_t *l1t, int M, int K, int rank,
-                              int group, uint8_t *qx, float *sx, uint16_t *T,
-                              void *stream);
+                              int group, int qfmt, uint8_t *qx, float *sx,
+                              uint16_t *T, void *stream);
 
 /* The W4A4 linear with fused low-rank up-projection and bias
  * [HF-SVDQ method and "Nunchaku Lite" paragraph]:
- *   P[g, m, n] = sum_{k in g} qx[m, k] qw[n, k]      (exact integer, i8 MFMA)
+ *   P[g, m, n] = sum_{k in g} qx[m, k] qw[n, k]      (exact: i8 MFMA for the
+ *                                                    INT4 container, FP6 MFMA
+ *                                                    for the FP6 container)
  *   acc[m, n]  = sum_g (sx[g, m] sw[g, n]) P[g, m, n] (fp32)
  *   y[m, n]    = acc + sum_j T[m, j] L2[j, n] + bias[n]  (bf16 MFMA, fp32)
  *   Y = y rounded once to bf16 (round to nearest even) or stored as fp32.
- * In:  qx [M, K/2], sx [K/64, M], T [M, rank] (NULL if rank 0),
- *      qw [N, K/2], sw [K/64, N], l2t [N, rank] (NULL if rank 0),
- *      bias [N] bf16 or NULL. y_dtype: SVDQ_BF16 or SVDQ_F32.
+ * In:  qx [M, R], sx [K/64, M], T [M, rank] (NULL if rank 0),
+ *      qw [N, R], sw [K/64, N], l2t [N, rank] (NULL if rank 0),
+ *      bias [N] bf16 or NULL; qfmt: the container of both qx and qw, whose
+ *      rows are R = svdq_qrow_bytes(K, qfmt) bytes. y_dtype: SVDQ_BF16 or
+ *      SVDQ_F32.
  * Out: Y [M, N] of y_dtype.
  * Shapes: M >= 0, K % 64 == 0, N % 8 == 0, rank % 16 == 0, rank <= 64.
  * Deterministic (no atomics; fixed summation order).
@@ -190,8 +222,8 @@ svdq_status svdq_w4a4_linear(const uint8_t *qx, const float *sx,
                              const uint16_t *T, const uint8_t *qw,
                              const float *sw, const uint16_t *l2t,
                              const uint16_t *bias, int M, int N, int K,
-                             int rank, int group, void *Y, int y_dtype,
-                             void *stream);
+                             int rank, int group, int qfmt, void *Y,
+                             int y_dtype, void *stream);
 
 /* Bytes of device workspace w8a8_linear needs for an [M, K] input. */
 size_t w8a8_workspace_bytes(int M, int K);
@@ -215,10 +247,10 @@ svdq_status w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
 
 /* ------------------------------------------- TEST-ONLY (same kernels) --- */
 
-/* INT4 group partials from the W4A4 GEMM's own main loop:
+/* INT4 group partials from the W4A4 GEMM's own main loop (container qfmt):
  *   P[g, m, n] = sum_{k in g} qx[m, k] qw[n, k]  as int32, [K/64, M, N]. */
 svdq_status svdq_debug_group_partials(const uint8_t *qx, const uint8_t *qw,
-                                      int M, int N, int K, int group,
+                                      int M, int N, int K, int group, int qfmt,
                                       int32_t *P, void *stream);
 
 /* INT8 accumulators from the W8A8 GEMM's own main loop:

@@ -66,24 +66,47 @@ def make_problem(M, K, N, rank, seed=0, outliers=(), bias=True, zero_rows=()):
     return {"X": {"bits": Xb, "values": Xv}, "W": W, "bias": bvals, "prep": prep, "abi": sq.to_abi(prep)}
 
 
-def run_quantize_act(Xbits, abi, rank):
+FORMATS = [b.QFMT_INT4, b.QFMT_FP6]
+FORMAT_IDS = ["int4", "fp6"]
+
+
+def pack_codes(codes, qfmt):
+    """Oracle codes [rows, K] -> the container's bytes (test-side writers)."""
+    from tests.fp6_format import pack_fp6
+
+    return sq.pack_int4(codes) if qfmt == b.QFMT_INT4 else pack_fp6(codes)
+
+
+def unpack_codes(packed, K, qfmt):
+    from tests.fp6_format import unpack_fp6
+
+    return sq.unpack_int4(packed) if qfmt == b.QFMT_INT4 else unpack_fp6(packed, K)
+
+
+def weights_bytes(prep, abi, qfmt):
+    """The oracle's weight codes in container `qfmt` ([N, row bytes])."""
+    return abi["qw"] if qfmt == b.QFMT_INT4 else pack_codes(np.asarray(prep["qw"]).T, qfmt)
+
+
+def run_quantize_act(Xbits, abi, rank, qfmt=b.QFMT_INT4):
     t = torch()
     M, K = Xbits.shape
     Xd = dev(Xbits)
-    qx = t.empty((M, K // 2), dtype=t.uint8, device="cuda")
+    qx = t.empty((M, b.svdq_qrow_bytes(K, qfmt)), dtype=t.uint8, device="cuda")
     sx = t.empty((K // 64, M), dtype=t.float32, device="cuda")
     T = t.empty((M, max(rank, 1)), dtype=t.int16, device="cuda") if rank else None
     l1t = dev(abi["l1t"]) if rank else None
-    b.svdq_quantize_act(Xd, dev(abi["s"]), l1t, qx, sx, T, rank)
+    b.svdq_quantize_act(Xd, dev(abi["s"]), l1t, qx, sx, T, rank, qfmt=qfmt)
     t.cuda.synchronize()
     return qx, sx, T
 
 
-def run_linear(qx, sx, T, abi, bias_bits, M, N, K, rank, out="bf16"):
+def run_linear(qx, sx, T, abi, bias_bits, M, N, K, rank, out="bf16", qfmt=b.QFMT_INT4, qw_bytes=None):
     t = torch()
     Y = t.empty((M, N), dtype=t.float32 if out == "f32" else t.int16, device="cuda")
-    b.svdq_w4a4_linear(qx, sx, T, dev(abi["qw"]), dev(abi["sw"]), dev(abi["l2t"]) if rank else None,
-                       dev(bias_bits) if bias_bits is not None else None, Y, M, N, K, rank)
+    qw = abi["qw"] if qw_bytes is None else qw_bytes
+    b.svdq_w4a4_linear(qx, sx, T, dev(qw), dev(abi["sw"]), dev(abi["l2t"]) if rank else None,
+                       dev(bias_bits) if bias_bits is not None else None, Y, M, N, K, rank, qfmt=qfmt)
     t.cuda.synchronize()
     return Y
 

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert b.svdq_version() == 1
+    assert b.svdq_version() == 2
     for s in range(7):
         assert b.status_string(s)
     assert "unknown" in b.status_string(99)
@@ -55,9 +55,9 @@ def test_arch_override_fails_closed_before_launch():
     lib = b.lib()
     b.svdq_debug_set_arch_override("gfx942")
     try:
-        st = lib.svdq_quantize_act(FAKE, FAKE, FAKE, 16, 128, 16, 64, FAKE, FAKE, FAKE, None)
+        st = lib.svdq_quantize_act(FAKE, FAKE, FAKE, 16, 128, 16, 64, 0, FAKE, FAKE, FAKE, None)
         assert st == b.SVDQ_ERR_UNSUPPORTED_DEVICE
-        st = lib.svdq_w4a4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 64, 128, 16, 64,
+        st = lib.svdq_w4a4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 64, 128, 16, 64, 1,
                                   FAKE, b.SVDQ_BF16, None)
         assert st == b.SVDQ_ERR_UNSUPPORTED_DEVICE
         st = lib.w8a8_linear(FAKE, FAKE, 1.0, None, 16, 64, 128, FAKE, 1 << 20, FAKE, None)
@@ -77,21 +77,25 @@ def test_arch_override_fails_closed_before_launch():
 ])
 def test_quantize_act_shape_checks(args, expected):
     M, K, rank, group = args
-    st = b.lib().svdq_quantize_act(FAKE, FAKE, FAKE, M, K, rank, group, FAKE, FAKE, FAKE, None)
+    st = b.lib().svdq_quantize_act(FAKE, FAKE, FAKE, M, K, rank, group, 0, FAKE, FAKE, FAKE, None)
     assert st == expected
 
 
 def test_null_and_misaligned_pointers_rejected():
     lib = b.lib()
-    assert lib.svdq_quantize_act(None, FAKE, FAKE, 16, 128, 16, 64, FAKE, FAKE, FAKE, None) == \
+    assert lib.svdq_quantize_act(None, FAKE, FAKE, 16, 128, 16, 64, 0, FAKE, FAKE, FAKE, None) == \
         b.SVDQ_ERR_INVALID_ARGUMENT
-    assert lib.svdq_quantize_act(MISALIGNED, FAKE, FAKE, 16, 128, 16, 64, FAKE, FAKE, FAKE, None) == \
+    assert lib.svdq_quantize_act(MISALIGNED, FAKE, FAKE, 16, 128, 16, 64, 0, FAKE, FAKE, FAKE, None) == \
         b.SVDQ_ERR_MISALIGNED
-    assert lib.svdq_w4a4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 60, 128, 16, 64, FAKE,
+    assert lib.svdq_quantize_act(FAKE, FAKE, FAKE, 16, 128, 16, 64, 2, FAKE, FAKE, FAKE, None) == \
+        b.SVDQ_ERR_INVALID_ARGUMENT  # unknown container
+    assert lib.svdq_w4a4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 60, 128, 16, 64, 0, FAKE,
                                 b.SVDQ_BF16, None) == b.SVDQ_ERR_UNSUPPORTED_SHAPE  # N % 8
-    assert lib.svdq_w4a4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 64, 128, 16, 64, FAKE,
+    assert lib.svdq_w4a4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 64, 128, 16, 64, 0, FAKE,
                                 7, None) == b.SVDQ_ERR_INVALID_ARGUMENT  # dtype
-    assert lib.svdq_w4a4_linear(FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 16, 64, 128, 16, 64, FAKE,
+    assert lib.svdq_w4a4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 64, 128, 16, 64, 5, FAKE,
+                                b.SVDQ_BF16, None) == b.SVDQ_ERR_INVALID_ARGUMENT  # container
+    assert lib.svdq_w4a4_linear(FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 16, 64, 128, 16, 64, 1, FAKE,
                                 b.SVDQ_BF16, None) == b.SVDQ_ERR_INVALID_ARGUMENT  # T missing
     assert lib.w8a8_linear(FAKE, FAKE, 1.0, None, 16, 64, 128, FAKE, 16, FAKE, None) == \
         b.SVDQ_ERR_INVALID_ARGUMENT  # workspace too small
@@ -99,7 +103,7 @@ def test_null_and_misaligned_pointers_rejected():
         b.SVDQ_ERR_INVALID_ARGUMENT
     assert lib.w8a8_linear(FAKE, FAKE, 1.0, None, 16, 64, 133184, FAKE, 1 << 40, FAKE, None) == \
         b.SVDQ_ERR_UNSUPPORTED_SHAPE  # K 127^2 overflows int32
-    assert lib.svdq_debug_group_partials(FAKE, FAKE, 16, 64, 96, 64, FAKE, None) == \
+    assert lib.svdq_debug_group_partials(FAKE, FAKE, 16, 64, 96, 64, 0, FAKE, None) == \
         b.SVDQ_ERR_UNSUPPORTED_SHAPE
     assert lib.svdq_channel_absmax(FAKE, 4, 12, FAKE, None) == b.SVDQ_ERR_UNSUPPORTED_SHAPE
 
@@ -127,4 +131,34 @@ def test_host_prepare_rejects_bad_input():
     a2[0] = np.inf
     with pytest.raises(b.SvdqError) as e:
         b.svdq_prepare_weights(W, a2, 16)
+    assert e.value.status == b.SVDQ_ERR_NUMERICAL
+
+
+def test_row_bytes_of_the_containers():
+    assert b.svdq_qrow_bytes(3072, b.QFMT_INT4) == 1536
+    assert b.svdq_qrow_bytes(3072, b.QFMT_FP6) == 2304
+    assert b.svdq_qrow_bytes(100, b.QFMT_FP6) == 0
+    assert b.svdq_qrow_bytes(128, 9) == 0
+
+
+def test_repack_to_fp6_matches_the_documented_layout():
+    """The library's host repack vs the test-side FP6 writer built from the
+    header's description of the container (bit-exact)."""
+    from oracle import svdquant as sq
+    from tests.fp6_format import pack_fp6, unpack_fp6
+
+    rng = np.random.default_rng(12)
+    codes = rng.integers(-7, 8, (37, 320)).astype(np.int8)
+    codes[0, :] = 7
+    codes[1, :] = -7
+    codes[2, :] = 0
+    packed = sq.pack_int4(codes)
+    fp6 = b.svdq_repack_codes(packed, 320, b.QFMT_FP6)
+    assert np.array_equal(fp6, pack_fp6(codes))
+    assert np.array_equal(unpack_fp6(fp6, 320), codes)
+    assert np.array_equal(b.svdq_repack_codes(packed, 320, b.QFMT_INT4), packed)
+    bad = packed.copy()
+    bad[3, 0] = 0x08  # a nibble holding -8
+    with pytest.raises(b.SvdqError) as e:
+        b.svdq_repack_codes(bad, 320, b.QFMT_FP6)
     assert e.value.status == b.SVDQ_ERR_NUMERICAL
