@@ -18,12 +18,15 @@
 // and no integer-to-float conversion; the vector ALU does one multiply (the
 // scale product) and one FMA per output element and group.
 //
-// Block tile 256 (n) x 128 (m), 8 waves as 4 (n) x 2 (m), wave tile 64 x 64
-// (2 x 2 MFMA tiles of 32 x 32). Per group a block stages 256 x 48 + 128 x 48
-// bytes of codes (128-bit loads, rows padded to 56 bytes in LDS so that 32
-// lanes reading 8 bytes each from 32 rows hit distinct banks) and 384
-// scales; LDS is double buffered with one barrier per group and the next
-// group's loads in flight during the MFMAs.
+// Block tile 128 (n) x 128 (m), 4 waves as 2 x 2, wave tile 64 x 64 (2 x 2
+// MFMA tiles of 32 x 32); two blocks fit a CU. One LDS stage holds two
+// groups (K = 128): 128 x 96 code bytes of each operand and 2 x 256 scales.
+// Global loads are buffer loads with per-thread offsets computed once; rows
+// beyond M or N fall outside the buffer and read as zero, so the tails need
+// no branches. Each thread moves the same six 16-byte chunks per stage.
+// Staged rows are padded to 56 bytes so that 32 lanes reading 8 bytes from 32
+// consecutive rows touch distinct LDS banks. Stages are double buffered with
+// one barrier per stage, the next stage's loads in flight during the MFMAs.
 
 #include <hip/hip_runtime.h>
 
@@ -34,92 +37,37 @@ namespace svdq {
 
 namespace {
 
-constexpr int BN = 256;
+constexpr int BN = 128;
 constexpr int BM = 128;
-constexpr int THREADS = 512;
-constexpr int WAVES_N = 4;
-constexpr int WTN = 64;
-constexpr int WTM = 64;
-constexpr int ROW6 = 56;  // LDS stride of one staged row (48 code bytes + 8 pad)
-constexpr int CHUNKS_A = BN * 3;  // 16-byte chunks per group
-constexpr int CHUNKS = (BN + BM) * 3;
-constexpr int E8M0_X8 = 127 + 3;  // block scale 2^3
+constexpr int THREADS = 256;
+constexpr int KG = 2;            // groups per LDS stage
+constexpr int ROW6 = 56;         // LDS stride of one staged 48-byte row
+constexpr int GB = 48;           // code bytes per row and group
+constexpr int E8M0_X8 = 127 + 3; // MFMA block scale 2^3
+constexpr uint32_t kOob = 0x80000000u;  // an offset past any buffer
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 struct Stage6 {
-    uint8_t a[BN * ROW6];
-    uint8_t b[BM * ROW6];
-    float sa[BN];
-    float sb[BM];
+    uint8_t a[KG][BN * ROW6];
+    uint8_t b[KG][BM * ROW6];
+    float sa[KG][BN];
+    float sb[KG][BM];
 };
 
-struct Regs6 {
-    u32x4 c[3];
-    float s;
-};
-
-template <bool kLinear>
-__device__ __forceinline__ void load6(Regs6 &r, const uint8_t *__restrict__ qw, const uint8_t *__restrict__ qx,
-                                      const float *__restrict__ sw, const float *__restrict__ sx, int n0, int m0,
-                                      int N, int M, size_t R, int g) {
-    const int tid = threadIdx.x;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        const int c = tid + i * THREADS;
-        r.c[i] = zero;
-        if (c < CHUNKS_A) {
-            const int row = c / 3, part = c - 3 * (c / 3);
-            if (n0 + row < N)
-                r.c[i] = *reinterpret_cast<const u32x4 *>(qw + (size_t)(n0 + row) * R + (size_t)g * 48 + part * 16);
-        } else if (c < CHUNKS) {
-            const int cc = c - CHUNKS_A;
-            const int row = cc / 3, part = cc - 3 * (cc / 3);
-            if (m0 + row < M)
-                r.c[i] = *reinterpret_cast<const u32x4 *>(qx + (size_t)(m0 + row) * R + (size_t)g * 48 + part * 16);
-        }
-    }
-    r.s = 0.0f;
-    if constexpr (kLinear) {
-        if (tid < BM) {
-            if (m0 + tid < M) r.s = sx[(size_t)g * M + m0 + tid];
-        } else if (tid < BM + BN) {
-            const int j = tid - BM;
-            if (n0 + j < N) r.s = sw[(size_t)g * N + n0 + j];
-        }
-    }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-template <bool kLinear>
-__device__ __forceinline__ void store6(Stage6 &st, const Regs6 &r) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        const int c = tid + i * THREADS;
-        uint8_t *dst = nullptr;
-        if (c < CHUNKS_A) {
-            const int row = c / 3, part = c - 3 * (c / 3);
-            dst = st.a + row * ROW6 + part * 16;
-        } else if (c < CHUNKS) {
-            const int cc = c - CHUNKS_A;
-            const int row = cc / 3, part = cc - 3 * (cc / 3);
-            dst = st.b + row * ROW6 + part * 16;
-        }
-        if (dst) {
-            *reinterpret_cast<u32x2 *>(dst) = u32x2{r.c[i][0], r.c[i][1]};
-            *reinterpret_cast<u32x2 *>(dst + 8) = u32x2{r.c[i][2], r.c[i][3]};
-        }
-    }
-    if constexpr (kLinear) {
-        if (tid < BM)
-            st.sb[tid] = r.s;
-        else if (tid < BM + BN)
-            st.sa[tid - BM] = r.s;
-    }
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// 24 bytes (32 codes: lane half lh of the group) of one staged row
+__device__ __forceinline__ float buf_load4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// 24 bytes (the 32 codes of lane half lh) of one staged row
 __device__ __forceinline__ i32x8 frag6(const uint8_t *row_base, int lh) {
     const uint8_t *p = row_base + 24 * lh;
     const u32x2 x0 = *reinterpret_cast<const u32x2 *>(p);
@@ -129,7 +77,7 @@ __device__ __forceinline__ i32x8 frag6(const uint8_t *row_base, int lh) {
 }
 
 template <bool kLinear>
-__global__ __launch_bounds__(THREADS, 1) void w4a4_fp6_kernel(
+__global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
     const uint8_t *__restrict__ qx, const float *__restrict__ sx, const uint16_t *__restrict__ T,
     const uint8_t *__restrict__ qw, const float *__restrict__ sw, const uint16_t *__restrict__ l2t,
     const uint16_t *__restrict__ bias, int M, int N, int K, int rank, void *__restrict__ Y, bool y_f32,
@@ -140,14 +88,42 @@ __global__ __launch_bounds__(THREADS, 1) void w4a4_fp6_kernel(
     const int tile_m = blockIdx.x / tiles_n;
     const int n0 = tile_n * BN;
     const int m0 = tile_m * BM;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wn = wave % WAVES_N;
-    const int wm = wave / WAVES_N;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wn = wave & 1;
+    const int wm = wave >> 1;
     const int r32 = lane & 31;
     const int lh = lane >> 5;
     const int G = K / 64;
-    const size_t R = (size_t)K / 4 * 3;
+    const int S = (G + KG - 1) / KG;
+    const uint32_t R = (uint32_t)K / 4 * 3;
+
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * R);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(qx, (uint32_t)M * R);
+
+    // this thread's three chunks of each operand per stage: chunk c = tid +
+    // 256 i covers row c / 6, 16-byte part (c % 6) of the stage's 96 bytes
+    uint32_t goff_a[3], goff_b[3], lds_a[3], lds_b[3];
+    int slot[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int c = tid + THREADS * i;
+        const int row = c / 6, p = c - 6 * (c / 6);
+        const int j = p / 3, part = p - 3 * (p / 3);
+        slot[i] = j;
+        goff_a[i] = (uint32_t)(n0 + row) * R + (uint32_t)(j * GB + part * 16);
+        goff_b[i] = (uint32_t)(m0 + row) * R + (uint32_t)(j * GB + part * 16);
+        lds_a[i] = (uint32_t)(j * BN * ROW6 + row * ROW6 + part * 16);
+        lds_b[i] = (uint32_t)(j * BM * ROW6 + row * ROW6 + part * 16);
+    }
+    // scales: waves 0-1 stage sx (token side), waves 2-3 sw (weight side)
+    const int sel = __builtin_amdgcn_readfirstlane(tid >> 7);
+    const int sj = tid & 127;
+    const int sL = sel ? N : M;
+    const int sbase = sel ? n0 : m0;
+    const bool s_ok = sbase + sj < sL;
+    __amdgpu_buffer_rsrc_t rs = make_rsrc(sel ? (const void *)sw : (const void *)sx, (uint32_t)G * (uint32_t)sL * 4u);
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -158,55 +134,99 @@ __global__ __launch_bounds__(THREADS, 1) void w4a4_fp6_kernel(
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-    Regs6 regs;
-    load6<kLinear>(regs, qw, qx, sw, sx, n0, m0, N, M, R, 0);
-    store6<kLinear>(stage[0], regs);
+    u32x4 ra[3], rb[3];
+    float rsv[KG];
+    auto load_stage = [&](int s) {
+        const int g0 = s * KG;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const bool ok = g0 + slot[i] < G;
+            const uint32_t adv = (uint32_t)g0 * GB;
+            ra[i] = buf_load16(rw, ok ? goff_a[i] + adv : kOob);
+            rb[i] = buf_load16(rx, ok ? goff_b[i] + adv : kOob);
+        }
+        if constexpr (kLinear) {
+#pragma unroll
+            for (int q = 0; q < KG; ++q) {
+                const bool ok = s_ok && g0 + q < G;
+                const uint32_t off = ((uint32_t)(g0 + q) * (uint32_t)sL + (uint32_t)(sbase + sj)) * 4u;
+                rsv[q] = buf_load4f(rs, ok ? off : kOob);
+            }
+        }
+    };
+    auto store_stage = [&](Stage6 &st) {
+        uint8_t *a = &st.a[0][0];
+        uint8_t *bb = &st.b[0][0];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            *reinterpret_cast<u32x2 *>(a + lds_a[i]) = u32x2{ra[i][0], ra[i][1]};
+            *reinterpret_cast<u32x2 *>(a + lds_a[i] + 8) = u32x2{ra[i][2], ra[i][3]};
+            *reinterpret_cast<u32x2 *>(bb + lds_b[i]) = u32x2{rb[i][0], rb[i][1]};
+            *reinterpret_cast<u32x2 *>(bb + lds_b[i] + 8) = u32x2{rb[i][2], rb[i][3]};
+        }
+        if constexpr (kLinear) {
+#pragma unroll
+            for (int q = 0; q < KG; ++q) {
+                if (sel)
+                    st.sa[q][sj] = rsv[q];
+                else
+                    st.sb[q][sj] = rsv[q];
+            }
+        }
+    };
+
+    load_stage(0);
+    store_stage(stage[0]);
     __syncthreads();
 
-    for (int g = 0; g < G; ++g) {
-        const Stage6 &cur = stage[g & 1];
-        if (g + 1 < G) load6<kLinear>(regs, qw, qx, sw, sx, n0, m0, N, M, R, g + 1);
-
-        i32x8 a[2], b[2];
+    for (int s = 0; s < S; ++s) {
+        const Stage6 &cur = stage[s & 1];
+        if (s + 1 < S) load_stage(s + 1);
+        const int ng = min(KG, G - s * KG);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            a[i] = frag6(cur.a + (wn * WTN + i * 32 + r32) * ROW6, lh);
-            b[i] = frag6(cur.b + (wm * WTM + i * 32 + r32) * ROW6, lh);
-        }
+        for (int q = 0; q < KG; ++q) {
+            if (q >= ng) break;
+            i32x8 a[2], b[2];
 #pragma unroll
-        for (int in = 0; in < 2; ++in) {
+            for (int i = 0; i < 2; ++i) {
+                a[i] = frag6(cur.a[q] + (wn * 64 + i * 32 + r32) * ROW6, lh);
+                b[i] = frag6(cur.b[q] + (wm * 64 + i * 32 + r32) * ROW6, lh);
+            }
 #pragma unroll
-            for (int im = 0; im < 2; ++im) {
-                const f32x16 P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    a[in], b[im], zero16, 2, 2, 0, E8M0_X8, 0, E8M0_X8);
-                if constexpr (kLinear) {
-                    const float sxm = cur.sb[wm * WTM + im * 32 + r32];
+            for (int in = 0; in < 2; ++in) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&cur.sa[wn * WTN + in * 32 + 8 * q + 4 * lh]);
+                for (int im = 0; im < 2; ++im) {
+                    const f32x16 P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        a[in], b[im], zero16, 2, 2, 0, E8M0_X8, 0, E8M0_X8);
+                    if constexpr (kLinear) {
+                        const float sxm = cur.sb[q][wm * 64 + im * 32 + r32];
 #pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            acc[in][im][4 * q + t] = fmaf(sxm * s4[t], P[4 * q + t], acc[in][im][4 * q + t]);
-                    }
-                } else {
-                    const int m = m0 + wm * WTM + im * 32 + r32;
-                    if (m < M) {
+                        for (int qq = 0; qq < 4; ++qq) {
+                            const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&cur.sa[q][wn * 64 + in * 32 + 8 * qq + 4 * lh]);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int n = n0 + wn * WTN + in * 32 + 8 * q + 4 * lh;
-                            if (n < N) {
-                                i32x4 v;
+                            for (int t = 0; t < 4; ++t)
+                                acc[in][im][4 * qq + t] = fmaf(sxm * s4[t], P[4 * qq + t], acc[in][im][4 * qq + t]);
+                        }
+                    } else {
+                        const int g = s * KG + q;
+                        const int m = m0 + wm * 64 + im * 32 + r32;
+                        if (m < M) {
 #pragma unroll
-                                for (int t = 0; t < 4; ++t) v[t] = (int)P[4 * q + t];
-                                *reinterpret_cast<i32x4 *>(Pout + ((size_t)g * M + m) * N + n) = v;
+                            for (int qq = 0; qq < 4; ++qq) {
+                                const int n = n0 + wn * 64 + in * 32 + 8 * qq + 4 * lh;
+                                if (n < N) {
+                                    i32x4 v;
+#pragma unroll
+                                    for (int t = 0; t < 4; ++t) v[t] = (int)P[4 * qq + t];
+                                    *reinterpret_cast<i32x4 *>(Pout + ((size_t)g * M + m) * N + n) = v;
+                                }
                             }
                         }
                     }
                 }
             }
         }
-
-        if (g + 1 < G) store6<kLinear>(stage[(g + 1) & 1], regs);
+        if (s + 1 < S) store_stage(stage[(s + 1) & 1]);
         __syncthreads();
     }
 
@@ -215,8 +235,8 @@ __global__ __launch_bounds__(THREADS, 1) void w4a4_fp6_kernel(
             bf16x8 la[2], lb[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int n = n0 + wn * WTN + i * 32 + r32;
-                const int m = m0 + wm * WTM + i * 32 + r32;
+                const int n = n0 + wn * 64 + i * 32 + r32;
+                const int m = m0 + wm * 64 + i * 32 + r32;
                 u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
                 if (n < N) va = *reinterpret_cast<const u32x4 *>(l2t + (size_t)n * rank + kk + 8 * lh);
                 if (m < M) vb = *reinterpret_cast<const u32x4 *>(T + (size_t)m * rank + kk + 8 * lh);
@@ -231,8 +251,8 @@ __global__ __launch_bounds__(THREADS, 1) void w4a4_fp6_kernel(
 #pragma unroll
         for (int in = 0; in < 2; ++in) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * WTN + in * 32 + 8 * q + 4 * lh;
+            for (int qq = 0; qq < 4; ++qq) {
+                const int n = n0 + wn * 64 + in * 32 + 8 * qq + 4 * lh;
                 if (n >= N) continue;
                 float bv[4] = {0.f, 0.f, 0.f, 0.f};
                 if (bias) {
@@ -244,11 +264,11 @@ __global__ __launch_bounds__(THREADS, 1) void w4a4_fp6_kernel(
                 }
 #pragma unroll
                 for (int im = 0; im < 2; ++im) {
-                    const int m = m0 + wm * WTM + im * 32 + r32;
+                    const int m = m0 + wm * 64 + im * 32 + r32;
                     if (m >= M) continue;
                     float v[4];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * q + t] + bv[t];
+                    for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * qq + t] + bv[t];
                     if (y_f32) {
                         *reinterpret_cast<f32x4 *>(static_cast<float *>(Y) + (size_t)m * N + n) =
                             f32x4{v[0], v[1], v[2], v[3]};
