@@ -92,8 +92,10 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
                 *reinterpret_cast<u32x2 *>(qx + (size_t)m * (K / 2) + kb / 2) = u32x2{packed[0], packed[1]};
         } else {
             // FP6 container: each code c as FP6 E2M3 of value c / 8 (sign bit,
-            // zero exponent, 3-bit magnitude), 6-bit fields packed LSB-first;
-            // the lane's 16 codes fill bytes [12 quad, +12) of the group's 48
+            // zero exponent, 3-bit magnitude), 6-bit fields packed LSB-first
+            // into the 24 bytes H_h of its half h = quad / 2; this lane's 16
+            // codes are bytes [12 (quad % 2), +12) of H_h. In the group's 48
+            // bytes, H_h[0:16] sits at 16 h and H_h[16:24] at 32 + 8 h.
             uint32_t w[3] = {0u, 0u, 0u};
             if (scale != 0.0f) {
 #pragma unroll
@@ -108,10 +110,21 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
                 }
             }
             if (row_ok) {
-                uint32_t *dst = reinterpret_cast<uint32_t *>(qx + (size_t)m * (K / 4 * 3) + (size_t)g * 48 + 12 * quad);
-                dst[0] = w[0];
-                dst[1] = w[1];
-                dst[2] = w[2];
+                uint8_t *grp = qx + (size_t)m * (K / 4 * 3) + (size_t)g * 48;
+                const int h = quad >> 1;
+                uint32_t *d0, *d1, *d2;
+                if ((quad & 1) == 0) {
+                    d0 = reinterpret_cast<uint32_t *>(grp + 16 * h);
+                    d1 = d0 + 1;
+                    d2 = d0 + 2;
+                } else {
+                    d0 = reinterpret_cast<uint32_t *>(grp + 16 * h + 12);
+                    d1 = reinterpret_cast<uint32_t *>(grp + 32 + 8 * h);
+                    d2 = d1 + 1;
+                }
+                *d0 = w[0];
+                *d1 = w[1];
+                *d2 = w[2];
             }
         }
         if (row_ok && quad == 0) sx[(size_t)g * M + m] = scale;

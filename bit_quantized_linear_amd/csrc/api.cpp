@@ -71,6 +71,9 @@ svdq_status launched(hipError_t e) {
     return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
+// Buffer loads address each operand with 32-bit offsets.
+bool fits_buffer(int64_t rows, int64_t row_bytes) { return rows * row_bytes < ((int64_t)1 << 31); }
+
 // Shape rules shared by the W4A4 entry points.
 svdq_status check_w4a4_shape(int M, int K, int rank, int group) {
     if (M < 0 || K <= 0 || rank < 0) return SVDQ_ERR_INVALID_ARGUMENT;
@@ -220,6 +223,12 @@ svdq_status svdq_w4a4_linear(const uint8_t *qx, const float *sx,
     if (!aligned16(qx) || !aligned16(sx) || !aligned16(T) || !aligned16(qw) ||
         !aligned16(sw) || !aligned16(l2t) || !aligned16(bias) || !aligned16(Y))
         return SVDQ_ERR_MISALIGNED;
+    {
+        const int64_t rb = (int64_t)svdq_qrow_bytes(K, qfmt);
+        if (!fits_buffer(M, rb) || !fits_buffer(N, rb) || !fits_buffer(K / SVDQ_GROUP, 4LL * M) ||
+            !fits_buffer(K / SVDQ_GROUP, 4LL * N))
+            return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    }
     st = current_device_ok();
     if (st != SVDQ_OK) return st;
     if (M == 0) return SVDQ_OK;
@@ -265,6 +274,10 @@ svdq_status svdq_debug_group_partials(const uint8_t *qx, const uint8_t *qw,
     if (N % 8) return SVDQ_ERR_UNSUPPORTED_SHAPE;
     if (!qw || (M > 0 && (!qx || !P))) return SVDQ_ERR_INVALID_ARGUMENT;
     if (!aligned16(qx) || !aligned16(qw) || !aligned16(P)) return SVDQ_ERR_MISALIGNED;
+    {
+        const int64_t rb = (int64_t)svdq_qrow_bytes(K, qfmt);
+        if (!fits_buffer(M, rb) || !fits_buffer(N, rb)) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    }
     st = current_device_ok();
     if (st != SVDQ_OK) return st;
     if (M == 0) return SVDQ_OK;

@@ -409,8 +409,10 @@ svdq_status w8a8_prepare_impl(const uint16_t *W, int K, int N, int8_t *qw, float
     return SVDQ_OK;
 }
 
-// Canonical INT4 nibbles -> FP6 E2M3 container (code / 8: sign in bit 5,
-// |code| in bits 0-2), 64 codes per 48 bytes, 6-bit fields LSB-first.
+// Canonical INT4 nibbles -> FP6 container: each code c as FP6 E2M3 of c / 8
+// (sign in bit 5, |c| in bits 0-2); the codes of half h of a group packed
+// LSB-first into 24 bytes H_h; the group's 48 bytes are
+// H_0[0:16] | H_1[0:16] | H_0[16:24] | H_1[16:24].
 svdq_status repack_codes_impl(const uint8_t *q, int rows, int K, int qfmt, uint8_t *out) {
     const int64_t in_row = K / 2;
     if (qfmt == SVDQ_QFMT_INT4) {
@@ -423,18 +425,24 @@ svdq_status repack_codes_impl(const uint8_t *q, int rows, int K, int qfmt, uint8
         const uint8_t *src = q + r * in_row;
         uint8_t *dst = out + r * out_row;
         for (int g = 0; g < K / 64; ++g) {
-            uint64_t bits[6] = {0, 0, 0, 0, 0, 0};  // 384 bits
-            for (int k = 0; k < 64; ++k) {
-                const uint8_t byte = src[g * 32 + k / 2];
-                const int nib = (k & 1) ? (byte >> 4) : (byte & 0xF);
-                const int code = nib >= 8 ? nib - 16 : nib;
-                if (code == -8) bad = true;
-                const uint64_t v = (code < 0 ? 0x20u : 0u) | (uint64_t)(code < 0 ? -code : code);
-                const int bit = 6 * k;
-                bits[bit / 64] |= v << (bit % 64);
-                if (bit % 64 > 58) bits[bit / 64 + 1] |= v >> (64 - bit % 64);
+            for (int h = 0; h < 2; ++h) {
+                uint64_t bits[3] = {0, 0, 0};  // the 192 bits of H_h
+                for (int i = 0; i < 32; ++i) {
+                    const int k = 32 * h + i;
+                    const uint8_t byte = src[g * 32 + k / 2];
+                    const int nib = (k & 1) ? (byte >> 4) : (byte & 0xF);
+                    const int code = nib >= 8 ? nib - 16 : nib;
+                    if (code == -8) bad = true;
+                    const uint64_t v = (code < 0 ? 0x20u : 0u) | (uint64_t)(code < 0 ? -code : code);
+                    const int bit = 6 * i;
+                    bits[bit / 64] |= v << (bit % 64);
+                    if (bit % 64 > 58) bits[bit / 64 + 1] |= v >> (64 - bit % 64);
+                }
+                uint8_t half[24];
+                for (int b = 0; b < 24; ++b) half[b] = (uint8_t)(bits[b / 8] >> (8 * (b % 8)));
+                std::memcpy(dst + g * 48 + 16 * h, half, 16);
+                std::memcpy(dst + g * 48 + 32 + 8 * h, half + 16, 8);
             }
-            for (int b = 0; b < 48; ++b) dst[g * 48 + b] = (uint8_t)(bits[b / 8] >> (8 * (b % 8)));
         }
     }
     return bad ? SVDQ_ERR_NUMERICAL : SVDQ_OK;

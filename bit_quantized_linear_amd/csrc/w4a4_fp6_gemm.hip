@@ -19,14 +19,19 @@
 // scale product) and one FMA per output element and group.
 //
 // Block tile 128 (n) x 128 (m), 4 waves as 2 x 2, wave tile 64 x 64 (2 x 2
-// MFMA tiles of 32 x 32); two blocks fit a CU. One LDS stage holds two
-// groups (K = 128): 128 x 96 code bytes of each operand and 2 x 256 scales.
-// Global loads are buffer loads with per-thread offsets computed once; rows
-// beyond M or N fall outside the buffer and read as zero, so the tails need
-// no branches. Each thread moves the same six 16-byte chunks per stage.
-// Staged rows are padded to 56 bytes so that 32 lanes reading 8 bytes from 32
-// consecutive rows touch distinct LDS banks. Stages are double buffered with
-// one barrier per stage, the next stage's loads in flight during the MFMAs.
+// MFMA tiles of 32 x 32). One LDS stage holds two groups (K = 128): per
+// operand 128 rows x 96 bytes (the six 16-byte chunks of the row's two
+// groups) plus 2 x 256 scales. Operands and scales go straight from global
+// memory to LDS (buffer_load ... lds, 16 or 4 bytes per lane, lane l to
+// base + l * size): no registers, no LDS store instructions. Consecutive
+// lanes take consecutive chunks of memory (six per row), so loads coalesce.
+// Within a staged row the six chunks are rotated by one position for rows
+// with bit 3 set, which spreads the 16-byte operand reads of 16 consecutive
+// rows over all LDS banks. Rows beyond M or N fall outside their buffer and
+// arrive as zeros, so the tails need no branches. A lane half's 24-byte MFMA
+// operand is one 16-byte read of its plane and one 8-byte read of the shared
+// third plane. Stages are double buffered with one barrier per stage; the
+// next stage's loads are in flight during the current stage's MFMAs.
 
 #include <hip/hip_runtime.h>
 
@@ -41,39 +46,35 @@ constexpr int BN = 128;
 constexpr int BM = 128;
 constexpr int THREADS = 256;
 constexpr int KG = 2;            // groups per LDS stage
-constexpr int ROW6 = 56;         // LDS stride of one staged 48-byte row
-constexpr int GB = 48;           // code bytes per row and group
+constexpr int GB = 48;           // container bytes per row and group
 constexpr int E8M0_X8 = 127 + 3; // MFMA block scale 2^3
 constexpr uint32_t kOob = 0x80000000u;  // an offset past any buffer
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int ROWB = 96;  // staged bytes per row and stage (6 chunks)
 
 struct Stage6 {
-    uint8_t a[KG][BN * ROW6];
-    uint8_t b[KG][BM * ROW6];
+    uint8_t a[BN * ROWB];
+    uint8_t b[BM * ROWB];
     float sa[KG][BN];
     float sb[KG][BM];
 };
+
+// position of data chunk d (slot * 3 + plane) within staged row r
+__device__ __forceinline__ int chunk_pos(int d, int r) { return (d + 6 - ((r >> 3) & 1)) % 6; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-__device__ __forceinline__ float buf_load4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-
-// 24 bytes (the 32 codes of lane half lh) of one staged row
-__device__ __forceinline__ i32x8 frag6(const uint8_t *row_base, int lh) {
-    const uint8_t *p = row_base + 24 * lh;
-    const u32x2 x0 = *reinterpret_cast<const u32x2 *>(p);
-    const u32x2 x1 = *reinterpret_cast<const u32x2 *>(p + 8);
-    const u32x2 x2 = *reinterpret_cast<const u32x2 *>(p + 16);
-    return i32x8{(int)x0[0], (int)x0[1], (int)x1[0], (int)x1[1], (int)x2[0], (int)x2[1], 0, 0};
+// the 24-byte MFMA operand from a staged region; off16/off8 are the byte
+// offsets (within the region) of the lane's 16-byte and 8-byte pieces
+__device__ __forceinline__ i32x8 frag6(const uint8_t *region, int off16, int off8) {
+    const u32x4 x = *reinterpret_cast<const u32x4 *>(region + off16);
+    const u32x2 y = *reinterpret_cast<const u32x2 *>(region + off8);
+    return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], 0, 0};
 }
 
 template <bool kLinear>
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
     const int m0 = tile_m * BM;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave & 1;
     const int wm = wave >> 1;
     const int r32 = lane & 31;
@@ -101,29 +102,73 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
 
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * R);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(qx, (uint32_t)M * R);
+    const __amdgpu_buffer_rsrc_t rsw = make_rsrc(sw, (uint32_t)G * (uint32_t)N * 4u);
+    const __amdgpu_buffer_rsrc_t rsx = make_rsrc(sx, (uint32_t)G * (uint32_t)M * 4u);
 
-    // this thread's three chunks of each operand per stage: chunk c = tid +
-    // 256 i covers row c / 6, 16-byte part (c % 6) of the stage's 96 bytes
-    uint32_t goff_a[3], goff_b[3], lds_a[3], lds_b[3];
-    int slot[3];
+    // Per stage the block issues 24 operand loads (12 per operand, 1 KB of
+    // staged rows each) and 8 scale loads (side, slot, 64-entry half); wave w
+    // takes operand loads 6w .. 6w+5 and scale loads 2w, 2w+1. Lane l of an
+    // operand load fills staged chunk position c = 64 i + l: row c / 6,
+    // position c % 6, i.e. data chunk (pos + rot(row)) % 6.
+    uint32_t voff[6];
+    int vslot[6];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        const int c = tid + THREADS * i;
-        const int row = c / 6, p = c - 6 * (c / 6);
-        const int j = p / 3, part = p - 3 * (p / 3);
-        slot[i] = j;
-        goff_a[i] = (uint32_t)(n0 + row) * R + (uint32_t)(j * GB + part * 16);
-        goff_b[i] = (uint32_t)(m0 + row) * R + (uint32_t)(j * GB + part * 16);
-        lds_a[i] = (uint32_t)(j * BN * ROW6 + row * ROW6 + part * 16);
-        lds_b[i] = (uint32_t)(j * BM * ROW6 + row * ROW6 + part * 16);
+    for (int i = 0; i < 6; ++i) {
+        const int idx = wave * 6 + i;
+        const int op = idx / 12;
+        const int c = (idx % 12) * 64 + lane;
+        const int row = c / 6, pos = c % 6;
+        const int d = (pos + ((row >> 3) & 1)) % 6;
+        const int slot = d / 3, part = d % 3;
+        vslot[i] = slot;
+        voff[i] = (uint32_t)((op ? m0 : n0) + row) * R + (uint32_t)(slot * GB + part * 16);
     }
-    // scales: waves 0-1 stage sx (token side), waves 2-3 sw (weight side)
-    const int sel = __builtin_amdgcn_readfirstlane(tid >> 7);
-    const int sj = tid & 127;
-    const int sL = sel ? N : M;
-    const int sbase = sel ? n0 : m0;
-    const bool s_ok = sbase + sj < sL;
-    __amdgpu_buffer_rsrc_t rs = make_rsrc(sel ? (const void *)sw : (const void *)sx, (uint32_t)G * (uint32_t)sL * 4u);
+    uint32_t soff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int idx = wave * 2 + i;
+        const int side = idx / 4, half = idx % 2;
+        soff[i] = (uint32_t)((side ? n0 : m0) + half * 64 + lane) * 4u;
+    }
+    // byte offsets of this lane's operand pieces within a staged region:
+    // [tile][slot][0 = 16-byte piece of plane lh, 1 = 8-byte piece of plane 2]
+    int aoff[2][KG][2], boff[2][KG][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int ra = wn * 64 + i * 32 + r32;
+        const int rb = wm * 64 + i * 32 + r32;
+#pragma unroll
+        for (int q = 0; q < KG; ++q) {
+            aoff[i][q][0] = ra * ROWB + 16 * chunk_pos(3 * q + lh, ra);
+            aoff[i][q][1] = ra * ROWB + 16 * chunk_pos(3 * q + 2, ra) + 8 * lh;
+            boff[i][q][0] = rb * ROWB + 16 * chunk_pos(3 * q + lh, rb);
+            boff[i][q][1] = rb * ROWB + 16 * chunk_pos(3 * q + 2, rb) + 8 * lh;
+        }
+    }
+
+    auto issue_stage = [&](int s, Stage6 &st) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const int idx = wave * 6 + i;
+            const int op = idx / 12;
+            const bool ok = s * KG + vslot[i] < G;
+            const uint32_t off = ok ? voff[i] + (uint32_t)(s * KG * GB) : kOob;
+            uint8_t *dst = (op ? st.b : st.a) + (idx % 12) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rx : rw, (lds_void *)dst, 16, off, 0, 0, 0);
+        }
+        if constexpr (kLinear) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int idx = wave * 2 + i;
+                const int side = idx / 4, slot = (idx % 4) / 2, half = idx % 2;
+                const int g = s * KG + slot;
+                const uint32_t L = side ? (uint32_t)N : (uint32_t)M;
+                const uint32_t off = g < G ? soff[i] + (uint32_t)g * L * 4u : kOob;
+                float *dst = (side ? st.sa[slot] : st.sb[slot]) + half * 64;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(side ? rsw : rsx, (lds_void *)dst, 4, off, 0, 0, 0);
+            }
+        }
+    };
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -134,54 +179,13 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-    u32x4 ra[3], rb[3];
-    float rsv[KG];
-    auto load_stage = [&](int s) {
-        const int g0 = s * KG;
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            const bool ok = g0 + slot[i] < G;
-            const uint32_t adv = (uint32_t)g0 * GB;
-            ra[i] = buf_load16(rw, ok ? goff_a[i] + adv : kOob);
-            rb[i] = buf_load16(rx, ok ? goff_b[i] + adv : kOob);
-        }
-        if constexpr (kLinear) {
-#pragma unroll
-            for (int q = 0; q < KG; ++q) {
-                const bool ok = s_ok && g0 + q < G;
-                const uint32_t off = ((uint32_t)(g0 + q) * (uint32_t)sL + (uint32_t)(sbase + sj)) * 4u;
-                rsv[q] = buf_load4f(rs, ok ? off : kOob);
-            }
-        }
-    };
-    auto store_stage = [&](Stage6 &st) {
-        uint8_t *a = &st.a[0][0];
-        uint8_t *bb = &st.b[0][0];
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            *reinterpret_cast<u32x2 *>(a + lds_a[i]) = u32x2{ra[i][0], ra[i][1]};
-            *reinterpret_cast<u32x2 *>(a + lds_a[i] + 8) = u32x2{ra[i][2], ra[i][3]};
-            *reinterpret_cast<u32x2 *>(bb + lds_b[i]) = u32x2{rb[i][0], rb[i][1]};
-            *reinterpret_cast<u32x2 *>(bb + lds_b[i] + 8) = u32x2{rb[i][2], rb[i][3]};
-        }
-        if constexpr (kLinear) {
-#pragma unroll
-            for (int q = 0; q < KG; ++q) {
-                if (sel)
-                    st.sa[q][sj] = rsv[q];
-                else
-                    st.sb[q][sj] = rsv[q];
-            }
-        }
-    };
-
-    load_stage(0);
-    store_stage(stage[0]);
+    issue_stage(0, stage[0]);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int s = 0; s < S; ++s) {
         const Stage6 &cur = stage[s & 1];
-        if (s + 1 < S) load_stage(s + 1);
+        if (s + 1 < S) issue_stage(s + 1, stage[(s + 1) & 1]);
         const int ng = min(KG, G - s * KG);
 #pragma unroll
         for (int q = 0; q < KG; ++q) {
@@ -189,8 +193,8 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
             i32x8 a[2], b[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                a[i] = frag6(cur.a[q] + (wn * 64 + i * 32 + r32) * ROW6, lh);
-                b[i] = frag6(cur.b[q] + (wm * 64 + i * 32 + r32) * ROW6, lh);
+                a[i] = frag6(cur.a, aoff[i][q][0], aoff[i][q][1]);
+                b[i] = frag6(cur.b, boff[i][q][0], boff[i][q][1]);
             }
 #pragma unroll
             for (int in = 0; in < 2; ++in) {
@@ -226,7 +230,10 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
                 }
             }
         }
-        if (s + 1 < S) store_stage(stage[(s + 1) & 1]);
+        // the next stage's direct-to-LDS loads must have landed before anyone
+        // reads them, and everyone must be done with this stage before it is
+        // refilled
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
