@@ -18,11 +18,24 @@ dominant kernel (the GEMM) against the dense peak of the MFMA type it runs on
 (FP6); "pct_int8_roofline" gives the same throughput against the int8 MFMA
 peak. The W8A8 linear on the attention shape is timed the same way and
 reported under "w8a8".
+
+HBM traffic of the GEMM comes from two rocprofv3 counter runs (FETCH_SIZE,
+then WRITE_SIZE) of this script with --calibrate-copy, which adds a plain
+elementwise kernel of known size (a negation, N bytes in, N bytes out) whose
+counter readings give the scale from counter units to bytes:
+
+    bench.py --summarize-pmc DIR_FETCH DIR_WRITE  > profiles/<summary>.txt
+
+writes the summary that later runs read; it records a hash of the GEMM's
+sources, and `traffic` is null once those sources have changed.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -39,6 +52,13 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
 
 METRIC = "W4A4+lowrank linear TOPS & % int8 MFMA roofline at M=4608,K=3072,N=12288"
 
+CSRC = os.path.join(ROOT, "bit_quantized_linear_amd", "csrc")
+GEMM_SOURCES = ("w4a4_fp6_gemm.hip", "device_common.h")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "svdq_w4a4_linear_fp6_mlp_up_4608x3072x12288_traffic.txt")
+COPY_BYTES = 256 << 20  # calibration kernel: reads and writes this many bytes
+GEMM_KERNEL_KEY = "w4a4_fp6_kernel<true>"
+COPY_KERNEL_KEY = "neg_kernel"
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -50,7 +70,88 @@ def parse():
     p.add_argument("--no-w8a8", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=4608,
                    help="token rows of the workload the CPU oracle is timed on")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain elementwise kernel of known size (for counter runs)")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="print the traffic summary from two rocprofv3 --pmc output folders (no GPU)")
     return p.parse_args()
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_means(folder, counter):
+    """Mean per-dispatch value of `counter` for the GEMM and the calibration kernel."""
+    vals = {"gemm": [], "copy": []}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                name = r.get("Kernel_Name", "")
+                key = "gemm" if GEMM_KERNEL_KEY in name else "copy" if COPY_KERNEL_KEY in name else None
+                if key:
+                    vals[key].append(float(r["Counter_Value"]))
+    if not vals["gemm"] or not vals["copy"]:
+        raise SystemExit(f"{folder}: no {counter} rows for both kernels")
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Text summary of the GEMM's HBM traffic per launch (printed to stdout)."""
+    fe = _counter_means(fetch_dir, "FETCH_SIZE")
+    wr = _counter_means(write_dir, "WRITE_SIZE")
+    # the calibration kernel moves COPY_BYTES each way: counter units -> bytes
+    f_scale = COPY_BYTES / fe["copy"]
+    w_scale = COPY_BYTES / wr["copy"]
+    fetch_b = fe["gemm"] * f_scale
+    write_b = wr["gemm"] * w_scale
+    M, K, N, r = 4608, 3072, 12288, 32
+    algo = algorithmic_gemm_bytes(M, N, K, r)
+    lines = [
+        "# HBM traffic of svdq_w4a4_linear (FP6 container), mlp_up M=4608 K=3072 N=12288 rank=32",
+        f"kernel_source_sha256_16: {gemm_source_hash()}",
+        f"calibration: elementwise negation of {COPY_BYTES} bytes (reads and writes that many)",
+        f"FETCH_SIZE gemm mean per dispatch (counter units): {fe['gemm']:.1f}",
+        f"FETCH_SIZE calibration kernel (counter units): {fe['copy']:.1f}  -> {f_scale:.2f} bytes/unit",
+        f"WRITE_SIZE gemm mean per dispatch (counter units): {wr['gemm']:.1f}",
+        f"WRITE_SIZE calibration kernel (counter units): {wr['copy']:.1f}  -> {w_scale:.2f} bytes/unit",
+        f"fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+        f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+        f"algorithmic_bytes_per_launch: {algo}",
+        f"traffic_over_algorithmic: {(fetch_b + write_b) / algo:.3f}",
+    ]
+    print("\n".join(lines))
+
+
+def read_traffic_summary():
+    """(traffic bytes per launch, details) from the committed summary, or
+    (None, reason) when it is missing or the GEMM sources changed since."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None, "no counter summary"
+    kv = {}
+    with open(TRAFFIC_SUMMARY) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != gemm_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return float(kv["traffic_bytes_per_launch"]), {
+        "fetch_bytes": float(kv["fetch_bytes_per_launch"]), "write_bytes": float(kv["write_bytes_per_launch"]),
+        "source": os.path.relpath(TRAFFIC_SUMMARY, ROOT)}
+
+
+def algorithmic_gemm_bytes(M, N, K, r):
+    """Bytes the GEMM must move at least once: both FP6 code matrices (3/4
+    byte per code), both scale matrices, T and L2 (bf16), bias, bf16 Y."""
+    return (M + N) * (K // 4 * 3) + (K // 64) * (M + N) * 4 + (M + N) * r * 2 + N * 2 + M * N * 2
 
 
 def log(*a):
@@ -58,7 +159,8 @@ def log(*a):
 
 
 def time_steps(fns, steps, warmup):
-    """Run `fns` in order per step; returns (ms_per_step, [ms per fn per step]).
+    """Run `fns` in order per step; returns (ms_per_step, [ms per fn per step],
+    wall ms per step, [ms of each step]).
 
     The whole timed region is bracketed by a device synchronize on both sides;
     HIP events recorded between the launches on the same stream give each
@@ -85,7 +187,29 @@ def time_steps(fns, steps, warmup):
     wall = (time.perf_counter() - t0) * 1e3 / steps
     total = start.elapsed_time(end) / steps
     per = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps for i in range(len(fns))]
-    return total, per, wall
+    each = [ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)]
+    return total, per, wall, each
+
+
+def time_cold(fns, reps):
+    """Per-step ms with the 256 MB last-level cache flushed before each step
+    by writing a 1 GiB buffer (untimed); returns the list of step times."""
+    import torch
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    out = []
+    for _ in range(reps):
+        flush.fill_(1.0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for f in fns:
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    del flush
+    return out
 
 
 def cpu_baseline(case, X, W, bias, rows):
@@ -109,22 +233,31 @@ def cpu_baseline(case, X, W, bias, rows):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
         blas_threads = None
-    t0 = time.perf_counter()
-    sq.forward(Xs, prep, bias["values"], "bf16")
-    dt = time.perf_counter() - t0
+    # repeated until about 10 s of CPU work have been timed (at most 5 passes)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        sq.forward(Xs, prep, bias["values"], "bf16")
+        reps += 1
+        if time.perf_counter() - t0 >= 10.0 or reps == 5:
+            break
+    dt = (time.perf_counter() - t0) / reps
     ops = 2.0 * rows * N * K
     cores = len(os.sched_getaffinity(0))
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": blas_threads or cores,
-            "host_cores": cores, "kind": "oracle", "seconds": dt,
+            "host_cores": cores, "kind": "oracle", "seconds": dt, "passes": reps,
             "sample": f"oracle forward (numpy fp64: quantize, per-group exact dgemms, scales, "
-                      f"low-rank, bias) on the first {rows} of {case.M} token rows, K={K}, N={N}, r={r}"}
+                      f"low-rank, bias) on the first {rows} of {case.M} token rows, K={K}, N={N}, r={r}; "
+                      f"mean of {reps} passes"}
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the multi-GPU sharding is described in DESIGN.md)"}))
+        print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on one GPU only "
+                                   "(--gpus must be 1); there is no multi-GPU path"}))
         sys.exit(2)
     import torch
 
@@ -183,9 +316,10 @@ def main():
     def gemm4():
         b.svdq_w4a4_linear(qx, sx, T, qw_d, sw_d, l2_d, b_d, Y, M, N, K, r, qfmt=b.QFMT_INT4)
 
-    ms4, per4, _ = time_steps([act4, gemm4], args.steps, args.warmup)
+    ms4, per4, _, _ = time_steps([act4, gemm4], args.steps, args.warmup)
     log(f"[bench] int4 container: step {ms4:.4f} ms (act {per4[0]:.4f} ms, gemm {per4[1]:.4f} ms)")
-    ms, per, wall = time_steps([act6, gemm6], args.steps, args.warmup)
+    ms, per, wall, each = time_steps([act6, gemm6], args.steps, args.warmup)
+    cold = time_cold([act6, gemm6], max(5, min(args.steps, 20)))
     ops = 2.0 * M * N * K
     tops = ops / (ms * 1e-3) / 1e12
     gemm_tops = ops / (per[1] * 1e-3) / 1e12
@@ -193,6 +327,13 @@ def main():
     act_gbs = act_bytes / (per[0] * 1e-3) / 1e9
     y_finite = bool(torch.isfinite(Y.view(torch.bfloat16).float()).all().item())
     log(f"[bench] step {ms:.4f} ms (act {per[0]:.4f} ms, gemm {per[1]:.4f} ms) -> {tops:.1f} TOPS")
+    traffic, traffic_detail = read_traffic_summary()
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
 
     out = {
         "metric": METRIC,
@@ -205,7 +346,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes x int4 codes (FP6 MFMA, exact) + fp32 scales + bf16 low-rank, bf16 out",
+        "dtype": "int4",
+        "dtype_detail": "int4 x int4 codes multiplied exactly on the FP6 MFMA, fp32 group scaling and "
+                        "accumulation, bf16 low-rank branch, bf16 output",
         "data": "synthetic (seeded N(0,1) activations with outlier channels, N(0,0.02) weights "
                 "with heavy columns, random init; no checkpoint)",
         "config": {"workload": f"{case.name}: SVDQuant W4A4 linear M={M} K={K} N={N} rank={r} group=64",
@@ -224,8 +367,15 @@ def main():
                            "gemm_pct_int8_roofline": round(100.0 * ops / (per4[1] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)},
         "roofline": {"bound": "mfma", "kernel": "svdq_w4a4_linear (FP6 container)", "mfma_dtype": "fp6",
                      "achieved": round(gemm_tops, 2), "peak": FP6_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tops / FP6_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(gemm_tops / FP6_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "traffic_detail": traffic_detail,
+                     "algorithmic_bytes": algorithmic_gemm_bytes(M, N, K, r),
+                     "algorithmic_ops": ops},
         "wall_ms_per_step": round(wall, 5),
+        "step_ms_median": round(float(np.median(each)), 5),
+        "step_ms_min": round(float(np.min(each)), 5),
+        "cold_step_ms_median": round(float(np.median(cold)), 5),
+        "cold_step_ms_min": round(float(np.min(cold)), 5),
         "outputs_finite": y_finite,
     }
 
@@ -242,7 +392,7 @@ def main():
         def w8():
             b.w8a8_linear(X8d, qw8d, sw8, b8d, ws, Y8)
 
-        ms8, _, _ = time_steps([w8], args.steps, args.warmup)
+        ms8, _, _, _ = time_steps([w8], args.steps, args.warmup)
         ops8 = 2.0 * c8.M * c8.N * c8.K
         out["w8a8"] = {"workload": f"W8A8 tensorwise M={c8.M} K={c8.K} N={c8.N}",
                        "ms": round(ms8, 5), "TOPS": round(ops8 / (ms8 * 1e-3) / 1e12, 2),

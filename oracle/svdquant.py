@@ -16,7 +16,7 @@ bullet: the weights are stored in a grouped INT4 physical format.
 Together:  y = dequant(Q4(X / s) . Q4(R)) + (X / s) . L1 . L2 + bias,
 with R = diag(s) W - L1 L2 evaluated on the stored 16-bit factors.
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
   R1  smoothing s_k = a_k^alpha / w_k^(1-alpha), a_k = max_m |X[m,k]|,
       w_k = max_n |W[k,n]|, alpha = 0.5; s_k = 1 when a_k or w_k is 0.
   R2  activation statistics come from the activations being quantized

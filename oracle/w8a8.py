@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE (see ``oracle/__init__.py``).
 
 [KREA-SVDQ] section "Решение: INT8 и W4A4": the first fast format is INT8
 "tensorwise" -- one scale for a whole tensor -- run on the integer tensor
-units. Readings taken (also listed in the design doc):
+units. Readings taken where the pages are silent:
   W1  symmetric grid [-127, 127], scale = RN32(absmax / 127) over the whole
       tensor; the activation scale is taken per call from the X being
       multiplied (dynamic), the weight scale once at preparation (static);

@@ -90,6 +90,33 @@ def test_quantize_act_attention_projection_full(qfmt):
     check_T(T, sq.lowrank_down(X["values"], prep["L1s"]), X["values"], prep["L1s"])
 
 
+@pytest.mark.parametrize("qfmt", H.FORMATS, ids=H.FORMAT_IDS)
+@pytest.mark.parametrize("order", ["shuffled", "by_magnitude"])
+def test_quantize_act_every_bf16_value(order, qfmt):
+    """Every bf16 bit pattern whose quotient by the smoothing factor stays
+    finite (signed zeros, subnormals, normals up to 2^121) goes through the
+    smoothing divide, the group absmax and the code rounding once: codes and
+    scales bit-exact against the oracle's IEEE fp32 divisions. Shuffled, a
+    group mixes all magnitudes; ordered by magnitude, a group holds 64
+    neighbouring magnitudes and its codes cover the whole grid."""
+    say("quantize_act every bf16 value", order, qfmt)
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits >> 7) & 0xFF) < 0xF8
+    bits = np.where(finite, bits, np.uint16(0)).astype(np.uint16)
+    rng = np.random.default_rng(65536)
+    if order == "shuffled":
+        bits = rng.permutation(bits)
+    else:
+        bits = bits[np.argsort(bits & np.uint16(0x7FFF), kind="stable")]
+    bits = bits.reshape(512, 128)
+    vals = wl.f32_from_bf16_bits(bits)
+    s = rng.uniform(1.0 / 16, 16.0, size=128).astype(np.float32)
+    qx, sx, _ = H.run_quantize_act(bits, {"s": s}, 0, qfmt)
+    cx, csx = sq.quantize_activations(vals, s)
+    assert np.array_equal(H.host(sx), csx)
+    assert np.array_equal(H.host(qx), H.pack_codes(cx, qfmt))
+
+
 def test_channel_absmax_matches_oracle():
     t = H.torch()
     say("channel_absmax")
