@@ -89,7 +89,7 @@ typedef enum svdq_dtype {
  *      the third holding both halves' tails). Every INT4 code is exact in
  *      this form; gfx950's FP6 MFMA, which runs at twice the int8 rate, reads
  *      a half as one 16-byte and one 8-byte piece and returns each group's
- *      partial sum as an *      exact fp32 integer. */
+ *      partial sum as an exact fp32 integer. */
 typedef enum svdq_qformat {
     SVDQ_QFMT_INT4 = 0,
     SVDQ_QFMT_FP6 = 1
