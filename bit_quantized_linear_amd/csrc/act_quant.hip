@@ -27,12 +27,31 @@ constexpr int kActRows = 16;   // token rows per block (one 16x16 MFMA row tile)
 // rank tile (8 channels each); B comes from l1t with the same channel
 // mapping. The 8 waves' fp32 partial T tiles are summed in wave order through
 // LDS, so T is deterministic.
-template <bool kFp6>
+constexpr float kTinyGroup = 0x1p-100f;
+
+// fp32(a / b), correctly rounded, from r = fp64(1 / b) (correctly rounded):
+// d = fp64(a * r) is within 2^-52 (relative) of a / b. A quotient of two
+// fp32 values with 24-bit significands lies either exactly on an fp32 value
+// or at least 2^-49 (relative) away from every fp32 rounding boundary (a
+// midpoint has an odd 25-bit significand; a / b equal to or within 2^-49 of
+// one would need a 49-bit numerator), so d and a / b round to the same fp32
+// value. This holds while the result is a normal fp32 number or overflows;
+// results below 2^-126 can fall on a subnormal midpoint, which the caller
+// excludes (groups whose largest |x / s| is below 2^-100 use IEEE division,
+// and in any other group a subnormal x / s becomes code 0 whatever its
+// exact value, as it is below 7 * 2^-26 of the scale).
+__device__ __forceinline__ float quotient_fp32(float a, double r) {
+    return (float)((double)a * r);
+}
+
+template <bool kFp6, int RT>
 __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ smooth,
     const uint16_t *__restrict__ l1t, int M, int K, int rank,
     uint8_t *__restrict__ qx, float *__restrict__ sx, uint16_t *__restrict__ T) {
-    __shared__ float red[kActWaves][kActRows][SVDQ_MAX_RANK];
+    constexpr int kRT = RT > 0 ? RT : 1;  // rank tiles held (rank / 16, at least one array slot)
+    __shared__ float red[kActWaves][kActRows][16 * kRT];
+    __shared__ double rcp[kActWaves][SVDQ_GROUP];  // per wave: 1/s of its current group's channels
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -42,11 +61,11 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
     const int m = m0 + row;
     const bool row_ok = m < M;
     const int G = K / SVDQ_GROUP;
-    const int rtiles = rank >> 4;
+    constexpr int rtiles = RT;
 
-    f32x4 tacc[SVDQ_MAX_RANK / 16];
+    f32x4 tacc[kRT];
 #pragma unroll
-    for (int i = 0; i < SVDQ_MAX_RANK / 16; ++i) tacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kRT; ++i) tacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int g = wave; g < G; g += kActWaves) {
         const int kb = g * SVDQ_GROUP + quad * 16;
@@ -56,33 +75,58 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
             xa = p[0];
             xb = p[1];
         }
-        const f32x4 *sp = reinterpret_cast<const f32x4 *>(smooth + kb);
-        float xh[16];
+        // 1/s of the group's 64 channels, one fp64 division per lane, shared
+        // through this wave's slice of LDS
+        rcp[wave][lane] = 1.0 / (double)smooth[g * SVDQ_GROUP + lane];
+        __builtin_amdgcn_wave_barrier();
+        const double *rq = &rcp[wave][quad * 16];
+        float xb16[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const f32x4 s4 = sp[i];
             const uint32_t w0 = (i < 2) ? xa[2 * i] : xb[2 * (i - 2)];
             const uint32_t w1 = (i < 2) ? xa[2 * i + 1] : xb[2 * (i - 2) + 1];
-            // X_hat = fp32(X / s): IEEE division, round to nearest even
-            xh[4 * i + 0] = bf16_bits_to_f32(w0 & 0xFFFFu) / s4[0];
-            xh[4 * i + 1] = bf16_bits_to_f32(w0 >> 16) / s4[1];
-            xh[4 * i + 2] = bf16_bits_to_f32(w1 & 0xFFFFu) / s4[2];
-            xh[4 * i + 3] = bf16_bits_to_f32(w1 >> 16) / s4[3];
+            xb16[4 * i + 0] = bf16_bits_to_f32(w0 & 0xFFFFu);
+            xb16[4 * i + 1] = bf16_bits_to_f32(w0 >> 16);
+            xb16[4 * i + 2] = bf16_bits_to_f32(w1 & 0xFFFFu);
+            xb16[4 * i + 3] = bf16_bits_to_f32(w1 >> 16);
         }
+        // X_hat = fp32(X / s), the IEEE quotient, computed as
+        // fp32(double(x) * fp64(1/s)): see quotient_fp32 for why it is exact
+        float xh[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) xh[t] = quotient_fp32(xb16[t], rq[t]);
+        __builtin_amdgcn_wave_barrier();
         float amax = 0.0f;
 #pragma unroll
         for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(xh[t]));
         amax = fmaxf(amax, __shfl_xor(amax, 16));
         amax = fmaxf(amax, __shfl_xor(amax, 32));
+        if (amax < kTinyGroup) {
+            // below the range quotient_fp32 covers: plain IEEE divisions
+            // (all four lanes of the row take this branch together)
+            const f32x4 *sp = reinterpret_cast<const f32x4 *>(smooth + kb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 s4 = sp[i];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) xh[4 * i + t] = xb16[4 * i + t] / s4[t];
+            }
+            amax = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(xh[t]));
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+        }
         const float scale = amax / 7.0f;
-
+        // code = RNE(fp32(x_hat / scale)), the quotient again via fp64
+        const double rscale = scale != 0.0f ? 1.0 / (double)scale : 0.0;
         if constexpr (!kFp6) {
             // INT4 container: two's-complement nibbles, low nibble = even k
             uint32_t packed[2] = {0u, 0u};
             if (scale != 0.0f) {
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
-                    float q = rintf(xh[t] / scale);  // round half to even
+                    float q = rintf(quotient_fp32(xh[t], rscale));  // round half to even
                     q = fminf(7.0f, fmaxf(-7.0f, q));
                     const uint32_t nib = (uint32_t)((int)q) & 0xFu;
                     packed[t >> 3] |= nib << (4 * (t & 7));
@@ -100,7 +144,7 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
             if (scale != 0.0f) {
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
-                    float q = rintf(xh[t] / scale);  // round half to even
+                    float q = rintf(quotient_fp32(xh[t], rscale));  // round half to even
                     q = fminf(7.0f, fmaxf(-7.0f, q));
                     const int qi = (int)q;
                     const uint32_t v = (qi < 0 ? 0x20u : 0u) | (uint32_t)(qi < 0 ? -qi : qi);
@@ -134,7 +178,7 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
         for (int s = 0; s < 2; ++s) {
             const bf16x8 a = __builtin_bit_cast(bf16x8, s == 0 ? xa : xb);
 #pragma unroll
-            for (int rt = 0; rt < SVDQ_MAX_RANK / 16; ++rt) {
+            for (int rt = 0; rt < kRT; ++rt) {
                 if (rt < rtiles) {
                     const bf16x8 b = *reinterpret_cast<const bf16x8 *>(
                         l1t + (size_t)(rt * 16 + row) * K + kb + 8 * s);
@@ -148,7 +192,7 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
     // 16x16 output: lane holds column (lane % 16) = rank index within the
     // tile, rows 4 (lane / 16) + t
 #pragma unroll
-    for (int rt = 0; rt < SVDQ_MAX_RANK / 16; ++rt) {
+    for (int rt = 0; rt < kRT; ++rt) {
         if (rt < rtiles) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) red[wave][4 * quad + t][rt * 16 + row] = tacc[rt][t];
@@ -205,16 +249,29 @@ __global__ __launch_bounds__(256) void channel_absmax_kernel(const uint16_t *__r
 
 }  // namespace
 
+template <int RT>
+static void launch_act_rt(dim3 grid, hipStream_t stream, bool fp6, const uint16_t *X, const float *smooth,
+                          const uint16_t *l1t, int M, int K, int rank, uint8_t *qx, float *sx, uint16_t *T) {
+    if (fp6)
+        hipLaunchKernelGGL((quantize_act_kernel<true, RT>), grid, dim3(kActWaves * 64), 0, stream, X, smooth,
+                           l1t, M, K, rank, qx, sx, T);
+    else
+        hipLaunchKernelGGL((quantize_act_kernel<false, RT>), grid, dim3(kActWaves * 64), 0, stream, X, smooth,
+                           l1t, M, K, rank, qx, sx, T);
+}
+
 hipError_t launch_quantize_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M,
                                int K, int rank, int qfmt, uint8_t *qx, float *sx, uint16_t *T,
                                hipStream_t stream) {
     const dim3 grid((M + kActRows - 1) / kActRows);
-    if (qfmt == SVDQ_QFMT_FP6)
-        hipLaunchKernelGGL(quantize_act_kernel<true>, grid, dim3(kActWaves * 64), 0, stream, X, smooth, l1t,
-                           M, K, rank, qx, sx, T);
-    else
-        hipLaunchKernelGGL(quantize_act_kernel<false>, grid, dim3(kActWaves * 64), 0, stream, X, smooth, l1t,
-                           M, K, rank, qx, sx, T);
+    const bool fp6 = qfmt == SVDQ_QFMT_FP6;
+    switch (rank / 16) {  // rank % 16 == 0 and rank <= 64 are checked by the caller
+        case 0: launch_act_rt<0>(grid, stream, fp6, X, smooth, l1t, M, K, rank, qx, sx, T); break;
+        case 1: launch_act_rt<1>(grid, stream, fp6, X, smooth, l1t, M, K, rank, qx, sx, T); break;
+        case 2: launch_act_rt<2>(grid, stream, fp6, X, smooth, l1t, M, K, rank, qx, sx, T); break;
+        case 3: launch_act_rt<3>(grid, stream, fp6, X, smooth, l1t, M, K, rank, qx, sx, T); break;
+        default: launch_act_rt<4>(grid, stream, fp6, X, smooth, l1t, M, K, rank, qx, sx, T); break;
+    }
     return hipGetLastError();
 }
 
