@@ -50,6 +50,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return u >> 16;
 }
 
+// Two fp32 -> packed bf16 (a in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950. Same result as f32_to_bf16_bits for every
+// non-NaN input.
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 template <class T>
 __device__ __forceinline__ T bitcast(const void *p) {
     return *reinterpret_cast<const T *>(p);

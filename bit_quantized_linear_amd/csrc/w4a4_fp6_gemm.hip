@@ -146,15 +146,26 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
         }
     }
 
+    // A full stage (both groups inside K) adds the same offset to every lane:
+    // it goes into the scalar offset, the per-lane offsets stay fixed, and
+    // rows past M or N stay out of range through their per-lane offset
+    // alone. Only a trailing half stage (odd group count) selects per lane:
+    // its second group would read past the end of the last row.
     auto issue_stage = [&](int s, Stage6 &st) {
+        const bool full = s * KG + KG <= G;
 #pragma unroll
         for (int i = 0; i < 6; ++i) {
             const int idx = wave * 6 + i;
             const int op = idx / 12;
-            const bool ok = s * KG + vslot[i] < G;
-            const uint32_t off = ok ? voff[i] + (uint32_t)(s * KG * GB) : kOob;
             uint8_t *dst = (op ? st.b : st.a) + (idx % 12) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rx : rw, (lds_void *)dst, 16, off, 0, 0, 0);
+            if (full) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rx : rw, (lds_void *)dst, 16, voff[i],
+                                                         s * KG * GB, 0, 0);
+            } else {
+                const bool ok = s * KG + vslot[i] < G;
+                const uint32_t off = ok ? voff[i] + (uint32_t)(s * KG * GB) : kOob;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rx : rw, (lds_void *)dst, 16, off, 0, 0, 0);
+            }
         }
         if constexpr (kLinear) {
 #pragma unroll
@@ -162,10 +173,12 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
                 const int idx = wave * 2 + i;
                 const int side = idx / 4, slot = (idx % 4) / 2, half = idx % 2;
                 const int g = s * KG + slot;
-                const uint32_t L = side ? (uint32_t)N : (uint32_t)M;
-                const uint32_t off = g < G ? soff[i] + (uint32_t)g * L * 4u : kOob;
+                const int L = side ? N : M;
                 float *dst = (side ? st.sa[slot] : st.sb[slot]) + half * 64;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(side ? rsw : rsx, (lds_void *)dst, 4, off, 0, 0, 0);
+                // a group past K is never read: no load at all
+                if (g < G)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(side ? rsw : rsx, (lds_void *)dst, 4, soff[i],
+                                                             g * L * 4, 0, 0);
             }
         }
     };
@@ -280,8 +293,8 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
                         *reinterpret_cast<f32x4 *>(static_cast<float *>(Y) + (size_t)m * N + n) =
                             f32x4{v[0], v[1], v[2], v[3]};
                     } else {
-                        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                        const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        const uint32_t lo = bf16x2_bits(v[0], v[1]);
+                        const uint32_t hi = bf16x2_bits(v[2], v[3]);
                         *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(Y) + (size_t)m * N + n) = u32x2{lo, hi};
                     }
                 }

@@ -163,8 +163,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void w4a4_gemm_kernel(
                         *reinterpret_cast<f32x4 *>(static_cast<float *>(Y) + (size_t)m * N + n) =
                             f32x4{v[0], v[1], v[2], v[3]};
                     } else {
-                        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                        const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        const uint32_t lo = bf16x2_bits(v[0], v[1]);
+                        const uint32_t hi = bf16x2_bits(v[2], v[3]);
                         *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(Y) + (size_t)m * N + n) = u32x2{lo, hi};
                     }
                 }

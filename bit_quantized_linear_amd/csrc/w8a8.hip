@@ -153,8 +153,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void w8a8_gemm_kernel(
                     float v[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) v[t] = (float)P[in][im][4 * q + t] * scale + bv[t];
-                    const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                    const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                    const uint32_t lo = bf16x2_bits(v[0], v[1]);
+                    const uint32_t hi = bf16x2_bits(v[2], v[3]);
                     *reinterpret_cast<u32x2 *>(Y + (size_t)m * N + n) = u32x2{lo, hi};
                 } else {
                     i32x4 v;
