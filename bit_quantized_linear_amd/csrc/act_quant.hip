@@ -138,8 +138,9 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
             // FP6 container: each code c as FP6 E2M3 of value c / 8 (sign bit,
             // zero exponent, 3-bit magnitude), 6-bit fields packed LSB-first
             // into the 24 bytes H_h of its half h = quad / 2; this lane's 16
-            // codes are bytes [12 (quad % 2), +12) of H_h. In the group's 48
-            // bytes, H_h[0:16] sits at 16 h and H_h[16:24] at 32 + 8 h.
+            // codes are bytes [12 (quad % 2), +12) of H_h. In the row's 48
+            // bytes of the group, H_h[0:16] sits at 16 h and H_h[16:24] at
+            // 32 + 8 h.
             uint32_t w[3] = {0u, 0u, 0u};
             if (scale != 0.0f) {
 #pragma unroll
@@ -154,7 +155,11 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
                 }
             }
             if (row_ok) {
-                uint8_t *grp = qx + (size_t)m * (K / 4 * 3) + (size_t)g * 48;
+                // blocks of 128 rows; inside a block, group g's rows follow
+                // one another (48 bytes each) after the block's earlier groups
+                const int b0 = m & ~127;
+                const int nb = min(128, M - b0);
+                uint8_t *grp = qx + (size_t)b0 * (K / 4 * 3) + ((size_t)g * nb + (m - b0)) * 48;
                 const int h = quad >> 1;
                 uint32_t *d0, *d1, *d2;
                 if ((quad & 1) == 0) {

@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int kMaxDevices = 64;
 
 std::mutex g_mutex;

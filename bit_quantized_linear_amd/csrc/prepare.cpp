@@ -412,7 +412,9 @@ svdq_status w8a8_prepare_impl(const uint16_t *W, int K, int N, int8_t *qw, float
 // Canonical INT4 nibbles -> FP6 container: each code c as FP6 E2M3 of c / 8
 // (sign in bit 5, |c| in bits 0-2); the codes of half h of a group packed
 // LSB-first into 24 bytes H_h; the group's 48 bytes are
-// H_0[0:16] | H_1[0:16] | H_0[16:24] | H_1[16:24].
+// H_0[0:16] | H_1[0:16] | H_0[16:24] | H_1[16:24]. Rows go in blocks of 128
+// (the last holds what is left); inside a block the groups follow one
+// another, each [rows of the block][48 bytes].
 svdq_status repack_codes_impl(const uint8_t *q, int rows, int K, int qfmt, uint8_t *out) {
     const int64_t in_row = K / 2;
     if (qfmt == SVDQ_QFMT_INT4) {
@@ -423,8 +425,12 @@ svdq_status repack_codes_impl(const uint8_t *q, int rows, int K, int qfmt, uint8
     bool bad = false;
     for (int r = 0; r < rows; ++r) {
         const uint8_t *src = q + r * in_row;
-        uint8_t *dst = out + r * out_row;
+        // blocks of 128 rows, groups one after another inside a block
+        const int64_t b0 = (int64_t)(r / 128) * 128;
+        const int64_t nb = std::min<int64_t>(128, rows - b0);
+        uint8_t *blk = out + b0 * out_row + (r - b0) * 48;
         for (int g = 0; g < K / 64; ++g) {
+            uint8_t *dst = blk + (int64_t)g * nb * 48;  // group g, row r of the block
             for (int h = 0; h < 2; ++h) {
                 uint64_t bits[3] = {0, 0, 0};  // the 192 bits of H_h
                 for (int i = 0; i < 32; ++i) {
@@ -440,8 +446,8 @@ svdq_status repack_codes_impl(const uint8_t *q, int rows, int K, int qfmt, uint8
                 }
                 uint8_t half[24];
                 for (int b = 0; b < 24; ++b) half[b] = (uint8_t)(bits[b / 8] >> (8 * (b % 8)));
-                std::memcpy(dst + g * 48 + 16 * h, half, 16);
-                std::memcpy(dst + g * 48 + 32 + 8 * h, half + 16, 8);
+                std::memcpy(dst + 16 * h, half, 16);
+                std::memcpy(dst + 32 + 8 * h, half + 16, 8);
             }
         }
     }

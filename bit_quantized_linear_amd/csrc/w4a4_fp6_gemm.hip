@@ -20,18 +20,22 @@
 //
 // Block tile 128 (n) x 128 (m), 4 waves as 2 x 2, wave tile 64 x 64 (2 x 2
 // MFMA tiles of 32 x 32). One LDS stage holds two groups (K = 128): per
-// operand 128 rows x 96 bytes (the six 16-byte chunks of the row's two
-// groups) plus 2 x 256 scales. Operands and scales go straight from global
-// memory to LDS (buffer_load ... lds, 16 or 4 bytes per lane, lane l to
-// base + l * size): no registers, no LDS store instructions. Consecutive
-// lanes take consecutive chunks of memory (six per row), so loads coalesce.
-// Within a staged row the six chunks are rotated by one position for rows
-// with bit 3 set, which spreads the 16-byte operand reads of 16 consecutive
-// rows over all LDS banks. Rows beyond M or N fall outside their buffer and
-// arrive as zeros, so the tails need no branches. A lane half's 24-byte MFMA
-// operand is one 16-byte read of its plane and one 8-byte read of the shared
-// third plane. Stages are double buffered with one barrier per stage; the
-// next stage's loads are in flight during the current stage's MFMAs.
+// operand the two groups' [128 rows][48 bytes] tiles, exactly as the FP6
+// container stores them (rows in blocks of 128, each block's groups one after
+// another), plus the two groups' 2 x 128 scales. Operands and scales go
+// straight from global memory to LDS (buffer_load ... lds, 16 or 4 bytes per
+// lane, lane l to base + l * size): no registers, no LDS store instructions.
+// A stage's operand tile is 6 KB of contiguous memory, copied 1 KB per load,
+// so every load is fully coalesced. Rows are 48 bytes apart, which already
+// spreads the 16-byte operand reads of 16 consecutive rows over all LDS
+// banks. In a block holding fewer than 128 rows (the tail of M or N) the
+// load runs on into the next tile or past the end of the buffer, where it
+// reads zeros (the whole offset is in the per-lane offset, so the range
+// check sees it); the extra rows only feed outputs that are never stored. A
+// lane half's 24-byte MFMA operand is one 16-byte read of its plane and one
+// 8-byte read of the shared third plane. Stages are double buffered with one
+// barrier per stage; the next stage's loads are in flight during the current
+// stage's MFMAs.
 
 #include <hip/hip_runtime.h>
 
@@ -48,22 +52,18 @@ constexpr int THREADS = 256;
 constexpr int KG = 2;            // groups per LDS stage
 constexpr int GB = 48;           // container bytes per row and group
 constexpr int E8M0_X8 = 127 + 3; // MFMA block scale 2^3
-constexpr uint32_t kOob = 0x80000000u;  // an offset past any buffer
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int ROWB = 96;  // staged bytes per row and stage (6 chunks)
+constexpr int TILE = 128 * GB;  // one group of a 128-row block: 6 KB
 
 struct Stage6 {
-    uint8_t a[BN * ROWB];
-    uint8_t b[BM * ROWB];
+    uint8_t a[KG * TILE];  // [group][row][48 bytes]
+    uint8_t b[KG * TILE];
     float sa[KG][BN];
     float sb[KG][BM];
 };
-
-// position of data chunk d (slot * 3 + plane) within staged row r
-__device__ __forceinline__ int chunk_pos(int d, int r) { return (d + 6 - ((r >> 3) & 1)) % 6; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
@@ -105,24 +105,15 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
     const __amdgpu_buffer_rsrc_t rsw = make_rsrc(sw, (uint32_t)G * (uint32_t)N * 4u);
     const __amdgpu_buffer_rsrc_t rsx = make_rsrc(sx, (uint32_t)G * (uint32_t)M * 4u);
 
-    // Per stage the block issues 24 operand loads (12 per operand, 1 KB of
-    // staged rows each) and 8 scale loads (side, slot, 64-entry half); wave w
-    // takes operand loads 6w .. 6w+5 and scale loads 2w, 2w+1. Lane l of an
-    // operand load fills staged chunk position c = 64 i + l: row c / 6,
-    // position c % 6, i.e. data chunk (pos + rot(row)) % 6.
-    uint32_t voff[6];
-    int vslot[6];
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-        const int idx = wave * 6 + i;
-        const int op = idx / 12;
-        const int c = (idx % 12) * 64 + lane;
-        const int row = c / 6, pos = c % 6;
-        const int d = (pos + ((row >> 3) & 1)) % 6;
-        const int slot = d / 3, part = d % 3;
-        vslot[i] = slot;
-        voff[i] = (uint32_t)((op ? m0 : n0) + row) * R + (uint32_t)(slot * GB + part * 16);
-    }
+    // Per stage the block issues 24 operand loads (per operand and group one
+    // 6 KB tile, six 1 KB loads) and 8 scale loads (side, slot, 64-entry
+    // half); wave w loads tile w (operand w / 2, group w % 2 of the stage)
+    // and scale loads 2w, 2w+1.
+    const int op_w = wave >> 1, q_w = wave & 1;
+    const int rows_w = op_w ? M : N;
+    const int b0_w = op_w ? m0 : n0;                     // first row of the 128-row block
+    const uint32_t base_w = (uint32_t)b0_w * R;          // the block's first byte
+    const uint32_t tstride_w = (uint32_t)min(128, rows_w - b0_w) * GB;  // bytes per group in the block
     uint32_t soff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -130,7 +121,7 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
         const int side = idx / 4, half = idx % 2;
         soff[i] = (uint32_t)((side ? n0 : m0) + half * 64 + lane) * 4u;
     }
-    // byte offsets of this lane's operand pieces within a staged region:
+    // byte offsets of this lane's operand pieces within a staged operand:
     // [tile][slot][0 = 16-byte piece of plane lh, 1 = 8-byte piece of plane 2]
     int aoff[2][KG][2], boff[2][KG][2];
 #pragma unroll
@@ -139,46 +130,42 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
         const int rb = wm * 64 + i * 32 + r32;
 #pragma unroll
         for (int q = 0; q < KG; ++q) {
-            aoff[i][q][0] = ra * ROWB + 16 * chunk_pos(3 * q + lh, ra);
-            aoff[i][q][1] = ra * ROWB + 16 * chunk_pos(3 * q + 2, ra) + 8 * lh;
-            boff[i][q][0] = rb * ROWB + 16 * chunk_pos(3 * q + lh, rb);
-            boff[i][q][1] = rb * ROWB + 16 * chunk_pos(3 * q + 2, rb) + 8 * lh;
+            aoff[i][q][0] = q * TILE + ra * GB + 16 * lh;
+            aoff[i][q][1] = q * TILE + ra * GB + 32 + 8 * lh;
+            boff[i][q][0] = q * TILE + rb * GB + 16 * lh;
+            boff[i][q][1] = q * TILE + rb * GB + 32 + 8 * lh;
+            // Opaque to the compiler: otherwise it pairs the 8-byte reads of
+            // two tiles into one ds_read2 and then needs moves to place each
+            // half next to its 16-byte piece in the MFMA operand.
+            asm volatile("" : "+v"(aoff[i][q][1]));
+            asm volatile("" : "+v"(boff[i][q][1]));
         }
     }
 
-    // A full stage (both groups inside K) adds the same offset to every lane:
-    // it goes into the scalar offset, the per-lane offsets stay fixed, and
-    // rows past M or N stay out of range through their per-lane offset
-    // alone. Only a trailing half stage (odd group count) selects per lane:
-    // its second group would read past the end of the last row.
+    // Every offset is carried whole in the per-lane offset, so a load that
+    // runs past the end of its buffer is caught by the range check and
+    // reads zeros. A group past K is never read and not loaded.
     auto issue_stage = [&](int s, Stage6 &st) {
-        const bool full = s * KG + KG <= G;
+        const int g = s * KG + q_w;
+        if (g < G) {
+            const uint32_t t0 = base_w + (uint32_t)g * tstride_w + (uint32_t)lane * 16u;
+            uint8_t *dst = (op_w ? st.b : st.a) + q_w * TILE;
 #pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            const int idx = wave * 6 + i;
-            const int op = idx / 12;
-            uint8_t *dst = (op ? st.b : st.a) + (idx % 12) * 1024;
-            if (full) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rx : rw, (lds_void *)dst, 16, voff[i],
-                                                         s * KG * GB, 0, 0);
-            } else {
-                const bool ok = s * KG + vslot[i] < G;
-                const uint32_t off = ok ? voff[i] + (uint32_t)(s * KG * GB) : kOob;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rx : rw, (lds_void *)dst, 16, off, 0, 0, 0);
-            }
+            for (int i = 0; i < 6; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(op_w ? rx : rw, (lds_void *)(dst + i * 1024), 16,
+                                                         t0 + i * 1024, 0, 0, 0);
         }
         if constexpr (kLinear) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int idx = wave * 2 + i;
                 const int side = idx / 4, slot = (idx % 4) / 2, half = idx % 2;
-                const int g = s * KG + slot;
-                const int L = side ? N : M;
+                const int gs = s * KG + slot;
+                const uint32_t L = side ? (uint32_t)N : (uint32_t)M;
                 float *dst = (side ? st.sa[slot] : st.sb[slot]) + half * 64;
-                // a group past K is never read: no load at all
-                if (g < G)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(side ? rsw : rsx, (lds_void *)dst, 4, soff[i],
-                                                             g * L * 4, 0, 0);
+                if (gs < G)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(side ? rsw : rsx, (lds_void *)dst, 4,
+                                                             soff[i] + (uint32_t)gs * L * 4u, 0, 0, 0);
             }
         }
     };

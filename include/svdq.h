@@ -80,16 +80,25 @@ typedef enum svdq_dtype {
  *  SVDQ_QFMT_INT4: K/2 bytes per row; two's-complement nibbles, byte j holds
  *      k = 2j (low nibble) and k = 2j + 1 (high nibble). The compact,
  *      canonical layout; its GEMM unpacks nibbles to int8 for i8 MFMA.
- *  SVDQ_QFMT_FP6: 3K/4 bytes per row, 48 per group g of 64 codes. Each code
- *      c is an FP6 E2M3 number equal to c / 8 (bit 5 = sign, bits 0-2 = |c|,
- *      exponent field 0). The codes of half h (k = 32h .. 32h + 31) of the
- *      group are packed into 24 bytes H_h, code k in bits [6(k - 32h), +6)
- *      least significant bit first; the group's 48 bytes are then
- *      H_0[0:16] | H_1[0:16] | H_0[16:24] | H_1[16:24] (three 16-byte planes,
- *      the third holding both halves' tails). Every INT4 code is exact in
- *      this form; gfx950's FP6 MFMA, which runs at twice the int8 rate, reads
- *      a half as one 16-byte and one 8-byte piece and returns each group's
- *      partial sum as an exact fp32 integer. */
+ *  SVDQ_QFMT_FP6: 3K/4 bytes per row (rows * 3K/4 bytes in all), 48 per
+ *      row and group of 64 codes, arranged for coalesced tile loads:
+ *      - Rows go in blocks of 128; block b holds rows 128b .. 128b + n_b - 1
+ *        with n_b = min(128, rows - 128b) and starts at byte 128 b (3K/4).
+ *      - Inside a block the groups follow one another: group g of block b
+ *        starts at byte 128 b (3K/4) + g n_b 48, and its row r (0 <= r <
+ *        n_b) at + 48 r. So 128 rows x 2 groups of a block are contiguous.
+ *      - One row's group is 48 bytes: each code c is an FP6 E2M3 number
+ *        equal to c / 8 (bit 5 = sign, bits 0-2 = |c|, exponent field 0);
+ *        the codes of half h (k = 32h .. 32h + 31) are packed into 24 bytes
+ *        H_h, code k in bits [6(k - 32h), +6) least significant bit first;
+ *        the 48 bytes are H_0[0:16] | H_1[0:16] | H_0[16:24] | H_1[16:24]
+ *        (three 16-byte planes, the third holding both halves' tails).
+ *      Every INT4 code is exact in this form; gfx950's FP6 MFMA, which runs
+ *      at twice the int8 rate, reads a half as one 16-byte and one 8-byte
+ *      piece and returns each group's partial sum as an exact fp32 integer.
+ *      The layout depends on the total row count: a buffer of `rows` rows is
+ *      read and written as a whole (no sub-range of rows is a valid buffer).
+ */
 typedef enum svdq_qformat {
     SVDQ_QFMT_INT4 = 0,
     SVDQ_QFMT_FP6 = 1

@@ -4,7 +4,9 @@ FP6 E2M3 number c/8 (bit 5 the sign, bits 0-2 the magnitude |c|, exponent
 field zero: a subnormal of OCP FP6 E2M3); the codes of half h of a 64-code
 group are packed least-significant-bit first into 24 bytes H_h (code k at
 bits [6(k - 32h), +6)); the group's 48 bytes are
-H_0[0:16] | H_1[0:16] | H_0[16:24] | H_1[16:24].
+H_0[0:16] | H_1[0:16] | H_0[16:24] | H_1[16:24]. Rows go in blocks of 128
+(the last one holds what is left), and inside a block the groups follow one
+another, each as [rows of the block][48 bytes].
 Independent of the library's own packers."""
 
 import numpy as np
@@ -35,25 +37,38 @@ def _pack_halves(v):
     return words.astype("<u8").view(np.uint8).reshape(v.shape[:-1] + (24,))
 
 
+def _blocks(rows):
+    """(first row, row count) of each 128-row block."""
+    return [(b, min(128, rows - b)) for b in range(0, rows, 128)]
+
+
 def pack_fp6(codes):
-    """codes [rows, K] in [-7, 7] -> bytes [rows, 3K/4]."""
+    """codes [rows, K] in [-7, 7] -> bytes [rows, 3K/4] (a flat buffer in the
+    blocked order, shaped rows x row bytes)."""
     c = np.asarray(codes, dtype=np.int64)
     rows, K = c.shape
     G = K // 64
     v = (np.where(c < 0, 0x20, 0) | np.abs(c)).astype(np.uint64).reshape(rows, G, 2, 32)
     halves = _pack_halves(v)  # [rows, G, 2, 24]
-    out = np.zeros((rows, G, 48), dtype=np.uint8)
+    rowgrp = np.zeros((rows, G, 48), dtype=np.uint8)
     for h in range(2):
-        out[:, :, _POS[h]] = halves[:, :, h, :]
+        rowgrp[:, :, _POS[h]] = halves[:, :, h, :]
+    out = np.zeros(rows * G * 48, dtype=np.uint8)
+    for b0, nb in _blocks(rows):
+        blk = rowgrp[b0:b0 + nb].transpose(1, 0, 2)  # [G, nb, 48]
+        out[b0 * G * 48:(b0 + nb) * G * 48] = blk.reshape(-1)
     return out.reshape(rows, G * 48)
 
 
 def unpack_fp6(packed, K):
-    """bytes [rows, 3K/4] -> codes [rows, K] (values decoded as FP6 E2M3 x 8)."""
-    p = np.ascontiguousarray(packed, dtype=np.uint8)
-    rows = p.shape[0]
+    """bytes [rows, 3K/4] in the blocked order -> codes [rows, K] (values
+    decoded as FP6 E2M3 x 8)."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1)
     G = K // 64
-    grp = p.reshape(rows, G, 48)
+    rows = p.size // (G * 48)
+    grp = np.zeros((rows, G, 48), dtype=np.uint8)
+    for b0, nb in _blocks(rows):
+        grp[b0:b0 + nb] = p[b0 * G * 48:(b0 + nb) * G * 48].reshape(G, nb, 48).transpose(1, 0, 2)
     table = np.array([fp6_value(b) * 8.0 for b in range(64)])
     out = np.zeros((rows, G, 64), dtype=np.float64)
     for h in range(2):

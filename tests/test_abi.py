@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert b.svdq_version() == 2
+    assert b.svdq_version() == 3
     for s in range(7):
         assert b.status_string(s)
     assert "unknown" in b.status_string(99)
@@ -162,3 +162,25 @@ def test_repack_to_fp6_matches_the_documented_layout():
     with pytest.raises(b.SvdqError) as e:
         b.svdq_repack_codes(bad, 320, b.QFMT_FP6)
     assert e.value.status == b.SVDQ_ERR_NUMERICAL
+
+
+@pytest.mark.parametrize("rows,K", [(1, 64), (127, 128), (128, 192), (129, 320), (300, 384)])
+def test_fp6_container_blocks_of_128_rows(rows, K):
+    """Ragged row counts: library repack == test-side writer, and one code
+    lands where the header's formula puts it (block b at 128 b (3K/4), group
+    g of the block at + g n_b 48, row r at + 48 r, plane 0 byte 0)."""
+    from oracle import svdquant as sq
+    from tests.fp6_format import pack_fp6
+
+    rng = np.random.default_rng(rows * 1000 + K)
+    codes = rng.integers(-7, 8, (rows, K)).astype(np.int8)
+    fp6 = b.svdq_repack_codes(sq.pack_int4(codes), K, b.QFMT_FP6)
+    assert np.array_equal(fp6, pack_fp6(codes))
+    m, g = rows - 1, K // 64 - 1
+    one = np.zeros((rows, K), np.int8)
+    one[m, g * 64] = 3  # code 3 -> FP6 bits 0b000011 at bit 0 of H_0
+    flat = b.svdq_repack_codes(sq.pack_int4(one), K, b.QFMT_FP6).reshape(-1)
+    b0 = (m // 128) * 128
+    nb = min(128, rows - b0)
+    pos = b0 * (K // 4 * 3) + g * nb * 48 + (m - b0) * 48
+    assert flat[pos] == 3 and np.count_nonzero(flat) == 1
