@@ -253,6 +253,7 @@ svdq_status w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
     if (M < 0 || N <= 0 || K <= 0) return SVDQ_ERR_INVALID_ARGUMENT;
     if (K % 64 || N % 8) return SVDQ_ERR_UNSUPPORTED_SHAPE;
     if ((int64_t)K * 127 * 127 >= ((int64_t)1 << 31)) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    if (!fits_buffer(M, K) || !fits_buffer(N, K)) return SVDQ_ERR_UNSUPPORTED_SHAPE;
     if (!std::isfinite(sw) || sw < 0.0f) return SVDQ_ERR_INVALID_ARGUMENT;
     if (!qw || (M > 0 && (!X || !Y || !workspace))) return SVDQ_ERR_INVALID_ARGUMENT;
     if (M > 0 && workspace_bytes < svdq::w8a8_workspace_size(M, K)) return SVDQ_ERR_INVALID_ARGUMENT;
@@ -290,6 +291,7 @@ svdq_status w8a8_debug_acc(const int8_t *qx, const int8_t *qw, int M, int N,
                            int K, int32_t *acc, void *stream) {
     if (M < 0 || N <= 0 || K <= 0) return SVDQ_ERR_INVALID_ARGUMENT;
     if (K % 64 || N % 8) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    if (!fits_buffer(M, K) || !fits_buffer(N, K)) return SVDQ_ERR_UNSUPPORTED_SHAPE;
     if (!qw || (M > 0 && (!qx || !acc))) return SVDQ_ERR_INVALID_ARGUMENT;
     if (!aligned16(qx) || !aligned16(qw) || !aligned16(acc)) return SVDQ_ERR_MISALIGNED;
     svdq_status st = current_device_ok();

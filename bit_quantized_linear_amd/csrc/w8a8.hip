@@ -19,7 +19,6 @@
 #include <algorithm>
 
 #include "device_common.h"
-#include "gemm_int.h"
 #include "internal.h"
 
 namespace svdq {
@@ -89,26 +88,99 @@ __global__ __launch_bounds__(kQThreads) void w8_quantize_kernel(const uint16_t *
 
 enum class W8Epilogue { kLinear, kAcc };
 
+// The GEMM: C^T tile = A . B^T with A = weight rows (output columns n, K
+// contiguous int8) and B = activation code rows (tokens m), on gfx950
+// v_mfma_i32_32x32x32_i8 with int32 accumulation over all of K.
+//  - Block 128 (n) x 128 (m), 4 waves as 2 x 2, wave tile 64 x 64 (2 x 2
+//    MFMA tiles of 32 x 32).
+//  - One LDS stage is 128 bytes of K (k0 .. k0 + 127) for the block's 128
+//    rows of each operand: 16 KB each, double buffered (64 KB per block).
+//  - Operands go straight from global memory to LDS (buffer_load ... lds,
+//    16 bytes per lane, lane l to base + 16 l): 8 lanes cover one row's
+//    128 bytes, so every 1 KB load reads 8 whole cache lines.
+//  - In LDS the 16-byte chunk c of row r sits at chunk position
+//    c ^ ((r >> 1) & 7), so the 16-byte operand reads of 16 consecutive rows
+//    fall on distinct banks; a lane fetches the global chunk that belongs at
+//    the position it writes.
+//  - Rows past M or N and a trailing half stage (K % 128 == 64) read zeros:
+//    the whole offset is in the per-lane offset, so the buffer range check
+//    sees it, and chunks past K get an offset past every buffer.
+constexpr int W8_TILE = 128;    // rows per block and operand
+constexpr int W8_KS = 128;      // K bytes per stage
+constexpr int W8_THREADS = 256;
+constexpr uint32_t kW8Oob = 0x80000000u;
+
+struct W8Stage {
+    uint8_t a[W8_TILE * W8_KS];
+    uint8_t b[W8_TILE * W8_KS];
+};
+
+typedef __attribute__((address_space(3))) void w8_lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t w8_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 template <W8Epilogue kEpi>
-__global__ __launch_bounds__(kGemmThreads, 2) void w8a8_gemm_kernel(
+__global__ __launch_bounds__(W8_THREADS, 2) void w8a8_gemm_kernel(
     const int8_t *__restrict__ qx, const int8_t *__restrict__ qw, const float *__restrict__ sxp,
     float sw, const uint16_t *__restrict__ bias, int M, int N, int K, uint16_t *__restrict__ Y,
     int32_t *__restrict__ acc_out, int tiles_n) {
-    __shared__ GemmStage stage[2];
+    __shared__ W8Stage stage[2];
 
     const int tile_n = blockIdx.x % tiles_n;
     const int tile_m = blockIdx.x / tiles_n;
-    const int n0 = tile_n * kTileN;
-    const int m0 = tile_m * kTileM;
+    const int n0 = tile_n * W8_TILE;
+    const int m0 = tile_m * W8_TILE;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = wave & 1;
     const int wm = wave >> 1;
     const int r32 = lane & 31;
     const int lh = lane >> 5;
-    const int S = K / kKStep;
-    const uint8_t *A = reinterpret_cast<const uint8_t *>(qw);
-    const uint8_t *B = reinterpret_cast<const uint8_t *>(qx);
+    const int S = (K + W8_KS - 1) / W8_KS;
+
+    const __amdgpu_buffer_rsrc_t ra = w8_rsrc(qw, (uint32_t)N * (uint32_t)K);
+    const __amdgpu_buffer_rsrc_t rb = w8_rsrc(qx, (uint32_t)M * (uint32_t)K);
+
+    // Wave w issues loads 8w .. 8w + 7 of the stage's 32 (16 per operand):
+    // load j of an operand fills staged rows 8 j .. 8 j + 7; lane l writes
+    // row 8 j + l / 8 at chunk position l % 8.
+    const int op = wave >> 1;  // waves 0, 1: weights; 2, 3: activations
+    const int row0 = op ? m0 : n0;
+    uint32_t gbase[8];
+    int gchunk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int j = (wave & 1) * 8 + i;
+        const int r = j * 8 + lane / 8;
+        const int c = (lane % 8) ^ ((r >> 1) & 7);
+        gchunk[i] = c;
+        gbase[i] = (uint32_t)(row0 + r) * (uint32_t)K + (uint32_t)(c * 16);
+    }
+    auto issue_stage = [&](int s, W8Stage &st) {
+        const int k0 = s * W8_KS;
+        const bool half = k0 + W8_KS > K;  // trailing 64 bytes only
+        uint8_t *dst = (op ? st.b : st.a) + (wave & 1) * 8 * 1024;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t off = gbase[i] + (uint32_t)k0;
+            if (half && k0 + gchunk[i] * 16 >= K) off = kW8Oob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra, (w8_lds_void *)(dst + i * 1024), 16, off,
+                                                     0, 0, 0);
+        }
+    };
+    // this lane's operand reads: row, and chunk position of chunk c = 2 kk + lh
+    int ara[2], arb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        ara[i] = wn * 64 + i * 32 + r32;
+        arb[i] = wm * 64 + i * 32 + r32;
+    }
+    auto frag = [&](const uint8_t *base, int r, int kk) {
+        const int c = (2 * kk + lh) ^ ((r >> 1) & 7);
+        return *reinterpret_cast<const i32x4 *>(base + r * W8_KS + c * 16);
+    };
 
     i32x16 P[2][2];
 #pragma unroll
@@ -118,14 +190,30 @@ __global__ __launch_bounds__(kGemmThreads, 2) void w8a8_gemm_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) P[i][j][e] = 0;
 
-    StepRegs<false> regs;
-    load_step<false, false>(regs, A, B, nullptr, nullptr, n0, m0, N, M, K, 0);
-    store_step<false>(stage[0], regs);
+    issue_stage(0, stage[0]);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int s = 0; s < S; ++s) {
-        if (s + 1 < S) load_step<false, false>(regs, A, B, nullptr, nullptr, n0, m0, N, M, K, s + 1);
-        mma_step(stage[s & 1], wn, wm, P);
-        if (s + 1 < S) store_step<false>(stage[(s + 1) & 1], regs);
+        const W8Stage &cur = stage[s & 1];
+        if (s + 1 < S) issue_stage(s + 1, stage[(s + 1) & 1]);
+#pragma unroll
+        for (int kk = 0; kk < W8_KS / 32; ++kk) {
+            i32x4 a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                a[i] = frag(cur.a, ara[i], kk);
+                b[i] = frag(cur.b, arb[i], kk);
+            }
+#pragma unroll
+            for (int in = 0; in < 2; ++in)
+#pragma unroll
+                for (int im = 0; im < 2; ++im) P[in][im] = mfma_i8_32x32x32(a[in], b[im], P[in][im]);
+        }
+        // the next stage must have landed before anyone reads it, and
+        // everyone must be done with this one before it is refilled; the
+        // scheduling barrier keeps this stage's MFMAs above the wait
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
@@ -188,18 +276,18 @@ hipError_t launch_w8a8_linear(const uint16_t *X, const int8_t *qw, float sw, con
     int qblocks = (int)std::max<int64_t>(1, std::min<int64_t>(4096, (chunks + kQThreads - 1) / kQThreads));
     hipLaunchKernelGGL(w8_quantize_kernel, dim3(qblocks), dim3(kQThreads), 0, stream, X, chunks, partial,
                        nparts, scale, codes);
-    const int tiles_n = (N + kTileN - 1) / kTileN;
-    const int tiles_m = (M + kTileM - 1) / kTileM;
-    hipLaunchKernelGGL(w8a8_gemm_kernel<W8Epilogue::kLinear>, dim3(tiles_n * tiles_m), dim3(kGemmThreads),
+    const int tiles_n = (N + W8_TILE - 1) / W8_TILE;
+    const int tiles_m = (M + W8_TILE - 1) / W8_TILE;
+    hipLaunchKernelGGL(w8a8_gemm_kernel<W8Epilogue::kLinear>, dim3(tiles_n * tiles_m), dim3(W8_THREADS),
                        0, stream, codes, qw, scale, sw, bias, M, N, K, Y, nullptr, tiles_n);
     return hipGetLastError();
 }
 
 hipError_t launch_w8a8_acc(const int8_t *qx, const int8_t *qw, int M, int N, int K, int32_t *acc,
                            hipStream_t stream) {
-    const int tiles_n = (N + kTileN - 1) / kTileN;
-    const int tiles_m = (M + kTileM - 1) / kTileM;
-    hipLaunchKernelGGL(w8a8_gemm_kernel<W8Epilogue::kAcc>, dim3(tiles_n * tiles_m), dim3(kGemmThreads), 0,
+    const int tiles_n = (N + W8_TILE - 1) / W8_TILE;
+    const int tiles_m = (M + W8_TILE - 1) / W8_TILE;
+    hipLaunchKernelGGL(w8a8_gemm_kernel<W8Epilogue::kAcc>, dim3(tiles_n * tiles_m), dim3(W8_THREADS), 0,
                        stream, qx, qw, nullptr, 0.0f, nullptr, M, N, K, nullptr, acc, tiles_n);
     return hipGetLastError();
 }

@@ -249,7 +249,8 @@ size_t w8a8_workspace_bytes(int M, int K);
  * In:  X [M, K] bf16; qw [N, K] int8; sw (host value); bias [N] bf16 or NULL;
  *      workspace of at least w8a8_workspace_bytes(M, K) bytes (device,
  *      16-byte aligned; holds the int8 codes of X and the scale).
- * Out: Y [M, N] bf16. Shapes: K % 64 == 0, N % 8 == 0, K * 127^2 < 2^31.
+ * Out: Y [M, N] bf16. Shapes: K % 64 == 0, N % 8 == 0, K * 127^2 < 2^31,
+ *      M * K < 2^31 and N * K < 2^31.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, MISALIGNED, UNSUPPORTED_DEVICE,
  *      HIP. */
 svdq_status w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
