@@ -67,17 +67,29 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
 #pragma unroll
     for (int i = 0; i < kRT; ++i) tacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // X and the smoothing factor of the wave's next group are loaded one
+    // group ahead, so their latency overlaps the current group's work
+    u32x4 nxa = {0u, 0u, 0u, 0u}, nxb = {0u, 0u, 0u, 0u};
+    float ns = 1.0f;
+    auto load_next = [&](int g) {
+        if (g < G) {
+            if (row_ok) {
+                const u32x4 *p = reinterpret_cast<const u32x4 *>(X + (size_t)m * K + g * SVDQ_GROUP + quad * 16);
+                nxa = p[0];
+                nxb = p[1];
+            }
+            ns = smooth[g * SVDQ_GROUP + lane];
+        }
+    };
+    load_next(wave);
     for (int g = wave; g < G; g += kActWaves) {
         const int kb = g * SVDQ_GROUP + quad * 16;
-        u32x4 xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
-        if (row_ok) {
-            const u32x4 *p = reinterpret_cast<const u32x4 *>(X + (size_t)m * K + kb);
-            xa = p[0];
-            xb = p[1];
-        }
+        const u32x4 xa = nxa, xb = nxb;
+        const float sg = ns;
+        load_next(g + kActWaves);
         // 1/s of the group's 64 channels, one fp64 division per lane, shared
         // through this wave's slice of LDS
-        rcp[wave][lane] = 1.0 / (double)smooth[g * SVDQ_GROUP + lane];
+        rcp[wave][lane] = 1.0 / (double)sg;
         __builtin_amdgcn_wave_barrier();
         const double *rq = &rcp[wave][quad * 16];
         float xb16[16];
