@@ -196,22 +196,36 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
                 a[i] = frag6(cur.a, aoff[i][q][0], aoff[i][q][1]);
                 b[i] = frag6(cur.b, boff[i][q][0], boff[i][q][1]);
             }
+            if constexpr (kLinear) {
+                // tiles t = (in, im) in order (0,0) (0,1) (1,0) (1,1); the MFMA
+                // of tile t + 1 is issued before the rescale of tile t, so the
+                // rescale never waits for a just-issued MFMA
+                f32x16 P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0], b[0], zero16, 2, 2, 0,
+                                                                           E8M0_X8, 0, E8M0_X8);
 #pragma unroll
-            for (int in = 0; in < 2; ++in) {
+                for (int t = 0; t < 4; ++t) {
+                    const int in = t >> 1, im = t & 1;
+                    f32x16 Pn;
+                    if (t + 1 < 4)
+                        Pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[(t + 1) >> 1], b[(t + 1) & 1], zero16,
+                                                                             2, 2, 0, E8M0_X8, 0, E8M0_X8);
+                    const float sxm = cur.sb[q][wm * 64 + im * 32 + r32];
 #pragma unroll
-                for (int im = 0; im < 2; ++im) {
-                    const f32x16 P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        a[in], b[im], zero16, 2, 2, 0, E8M0_X8, 0, E8M0_X8);
-                    if constexpr (kLinear) {
-                        const float sxm = cur.sb[q][wm * 64 + im * 32 + r32];
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&cur.sa[q][wn * 64 + in * 32 + 8 * qq + 4 * lh]);
 #pragma unroll
-                        for (int qq = 0; qq < 4; ++qq) {
-                            const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&cur.sa[q][wn * 64 + in * 32 + 8 * qq + 4 * lh]);
+                        for (int u = 0; u < 4; ++u)
+                            acc[in][im][4 * qq + u] = fmaf(sxm * s4[u], P[4 * qq + u], acc[in][im][4 * qq + u]);
+                    }
+                    if (t + 1 < 4) P = Pn;
+                }
+            } else {
 #pragma unroll
-                            for (int t = 0; t < 4; ++t)
-                                acc[in][im][4 * qq + t] = fmaf(sxm * s4[t], P[4 * qq + t], acc[in][im][4 * qq + t]);
-                        }
-                    } else {
+                for (int in = 0; in < 2; ++in) {
+#pragma unroll
+                    for (int im = 0; im < 2; ++im) {
+                        const f32x16 P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            a[in], b[im], zero16, 2, 2, 0, E8M0_X8, 0, E8M0_X8);
                         const int g = s * KG + q;
                         const int m = m0 + wm * 64 + im * 32 + r32;
                         if (m < M) {
@@ -221,7 +235,7 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
                                 if (n < N) {
                                     i32x4 v;
 #pragma unroll
-                                    for (int t = 0; t < 4; ++t) v[t] = (int)P[4 * qq + t];
+                                    for (int u = 0; u < 4; ++u) v[u] = (int)P[4 * qq + u];
                                     *reinterpret_cast<i32x4 *>(Pout + ((size_t)g * M + m) * N + n) = v;
                                 }
                             }
