@@ -250,6 +250,25 @@ def cpu_baseline(case, X, W, bias, rows):
                       f"mean of {reps} passes"}
 
 
+def cpu_baseline_w8a8(case, X, W, bias):
+    """The W8A8 oracle, untuned, on the whole W8A8 workload (quantize X, exact
+    fp64 product of the codes, scale, bias, bf16), repeated until about 3 s."""
+    from oracle import w8a8 as o8
+
+    qw, sw = o8.prepare_weights(W["values"])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        o8.forward(X["values"], qw, sw, bias["values"])
+        reps += 1
+        if time.perf_counter() - t0 >= 3.0 or reps == 5:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    ops = 2.0 * case.M * case.N * case.K
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle", "seconds": dt, "passes": reps,
+            "sample": f"oracle W8A8 forward on the whole workload M={case.M} K={case.K} N={case.N}"}
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -286,8 +305,11 @@ def main():
     amax = torch.zeros(K, dtype=torch.float32, device="cuda")
     b.svdq_channel_absmax(Xd, amax)
     torch.cuda.synchronize()
-    prep = b.svdq_prepare_weights(W["bits"], amax.cpu().numpy(), r)
-    log(f"[bench] host prepare {time.perf_counter() - t0:.1f}s")
+    amax_h = amax.cpu().numpy()
+    t1 = time.perf_counter()
+    prep = b.svdq_prepare_weights(W["bits"], amax_h, r)
+    prep_s = time.perf_counter() - t1
+    log(f"[bench] host prepare {prep_s:.1f}s (calibration + prepare {time.perf_counter() - t0:.1f}s)")
 
     def up(a):
         a = np.ascontiguousarray(a)
@@ -398,11 +420,24 @@ def main():
                        "ms": round(ms8, 5), "TOPS": round(ops8 / (ms8 * 1e-3) / 1e12, 2),
                        "pct_int8_roofline": round(100.0 * ops8 / (ms8 * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)}
         log(f"[bench] w8a8 {ms8:.4f} ms")
+        if not args.no_cpu_baseline:
+            out["w8a8"]["cpu_baseline"] = cpu_baseline_w8a8(c8, X8, W8, b8)
+            log(f"[bench] w8a8 cpu baseline {out['w8a8']['cpu_baseline']['seconds']:.1f}s")
 
+    out["prepare"] = {"library_s": round(prep_s, 3),
+                      "what": "svdq_prepare_weights on the host: smoothing, rank-r SVD, bf16 factors, "
+                              "residual, INT4 group codes and scales"}
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle) on {args.cpu_rows} rows ...")
         out["cpu_baseline"] = cpu_baseline(case, X, W, bias, args.cpu_rows)
         log(f"[bench] cpu baseline {out['cpu_baseline']['seconds']:.1f}s")
+        from oracle import svdquant as sq
+
+        t1 = time.perf_counter()
+        sq.prepare_weights(W["values"], amax_h, r)
+        out["prepare"]["oracle_s"] = round(time.perf_counter() - t1, 3)
+        out["prepare"]["oracle_cores"] = len(os.sched_getaffinity(0))
+        log(f"[bench] oracle prepare {out['prepare']['oracle_s']:.1f}s")
     print(json.dumps(out), flush=True)
 
 

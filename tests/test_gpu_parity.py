@@ -315,6 +315,32 @@ def test_run_to_run_byte_identical(qfmt):
     assert res[0] == res[1] == res[2]
 
 
+@pytest.mark.parametrize("qfmt", H.FORMATS, ids=H.FORMAT_IDS)
+def test_one_activation_pass_feeds_several_projections(qfmt):
+    """Shared-input projections (attention Q, K and V): the smoothing comes
+    from the concatenated weight, one svdq_quantize_act feeds the GEMM of
+    each projection (its column slice of the prepared weight, packed on its
+    own) and the GEMM of the concatenation; all match the oracle of the
+    concatenated linear."""
+    M, K, Np, r = 200, 512, 136, 16
+    say("shared activation pass, three projections", (M, K, Np, r), qfmt)
+    p = H.make_problem(M, K, 3 * Np, r, seed=33, outliers=(5, 77))
+    prep, abi = p["prep"], p["abi"]
+    qx, sx, T = H.run_quantize_act(p["X"]["bits"], abi, r, qfmt)
+    ref = sq.forward(p["X"]["values"], prep, p["bias"]["values"], "bf16")
+    bias_bits = p["bias"]["bits"]
+    qw_codes = np.asarray(prep["qw"]).T  # [N, K]
+    for j in range(3):
+        cols = slice(j * Np, (j + 1) * Np)
+        part = {"sw": np.ascontiguousarray(abi["sw"][:, cols]), "l2t": np.ascontiguousarray(abi["l2t"][cols]),
+                "qw": np.ascontiguousarray(abi["qw"][cols])}
+        qw_j = H.pack_codes(qw_codes[cols], qfmt)
+        Y = H.run_linear(qx, sx, T, part, np.ascontiguousarray(bias_bits[cols]), M, Np, K, r, "bf16", qfmt, qw_j)
+        check_output(H.y_values(Y, "bf16"), ref["y"][:, cols])
+    Yall = H.run_linear(qx, sx, T, abi, bias_bits, M, 3 * Np, K, r, "bf16", qfmt, H.weights_bytes(prep, abi, qfmt))
+    check_output(H.y_values(Yall, "bf16"), ref["y"])
+
+
 def test_empty_batch_is_a_no_op():
     t = H.torch()
     say("M = 0")
