@@ -3,9 +3,9 @@
 TEST INFRASTRUCTURE (see ``oracle/__init__.py``).
 
 Pure Python, exact rational arithmetic (fractions.Fraction), one element at a
-time. It takes the same definitions as ``oracle.svdquant`` and
-``oracle.w8a8`` but shares none of their code and uses a different
-formulation where one exists:
+time. It takes the same definitions as ``oracle.svdquant``,
+``oracle.w8a8`` and ``oracle.w4a16`` but shares none of their code and uses
+a different formulation where one exists:
 
 * fp32 rounding through ``struct`` (the C float conversion, nearest-even);
 * bf16 rounding by exact rational comparison with the two neighbours;
@@ -182,3 +182,33 @@ def w8a8_forward(X, qw_kn, sw, bias):
                      (Fraction(bias[n]) if bias is not None else 0))
           for n in range(N)] for m in range(M)]
     return qx, sx, acc, y
+
+
+def w4a16_forward(X, W, bias, group=64):
+    """W4A16 linear element by element from the unquantized weight: each
+    column's K-groups quantized with ``quantize_group`` (grid [-7, 7]), then
+    y[m][n] = bf16(sum_k x[m][k] code[k][n] scale[k // G][n] + bias[n]) summed
+    exactly. Returns (qw [K][N], sw [G][N], y [M][N])."""
+    M, K = len(X), len(X[0])
+    N = len(W[0])
+    G = K // group
+    qw = [[0] * N for _ in range(K)]
+    sw = [[0.0] * N for _ in range(G)]
+    for n in range(N):
+        for g in range(G):
+            codes, scale = quantize_group([W[k][n] for k in range(g * group, (g + 1) * group)], 7)
+            for i, c in enumerate(codes):
+                qw[g * group + i][n] = c
+            sw[g][n] = scale
+    y = []
+    for m in range(M):
+        row = []
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(X[m][k]) * Fraction(qw[k][n]) * Fraction(sw[k // group][n])
+            if bias is not None:
+                acc += Fraction(bias[n])
+            row.append(bf16_exact(acc))
+        y.append(row)
+    return qw, sw, y
