@@ -46,6 +46,9 @@ SIGNATURES = {
     "svdq_w4a4_linear": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
     "w8a8_workspace_bytes": (_sz, [_i, _i]),
     "w8a8_linear": (_i, [_vp, _vp, _f, _vp, _i, _i, _i, _vp, _sz, _vp, _vp]),
+    "w4a16_weight_bytes": (_sz, [_i, _i]),
+    "w4a16_prepare_weights": (_i, [_vp, _i, _i, _i, _vp]),
+    "w4a16_linear": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "svdq_debug_group_partials": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "w8a8_debug_acc": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
     "svdq_debug_set_arch_override": (_i, [C.c_char_p]),
@@ -195,6 +198,22 @@ def w8a8_prepare_weights(W_bits):
     return qw, float(sw[0])
 
 
+def w4a16_weight_bytes(K, N) -> int:
+    return int(lib().w4a16_weight_bytes(K, N))
+
+
+def w4a16_prepare_weights(W_bits, group=GROUP):
+    """W4A16 weight container (uint8, w4a16_weight_bytes(K, N) bytes) of a
+    bf16 weight W [K, N]."""
+    W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    K, N = W_bits.shape
+    nbytes = w4a16_weight_bytes(K, N)
+    out = np.empty(max(nbytes, 1), np.uint8)
+    st = lib().w4a16_prepare_weights(_np_ptr(W_bits, np.uint16), K, N, group, out.ctypes.data)
+    _check("w4a16_prepare_weights", st)
+    return out[:nbytes]
+
+
 # ---------------------------------------------------------------- device --
 
 def svdq_channel_absmax(X, absmax, stream=None):
@@ -231,6 +250,14 @@ def w8a8_linear(X, qw, sw, bias, workspace, Y, stream=None):
                            _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
                            _dev_ptr(Y, 2), _stream(stream))
     _check("w8a8_linear", st)
+
+
+def w4a16_linear(X, packed, bias, Y, N, group=GROUP, stream=None):
+    """Y [M, N] bf16 = X [M, K] bf16 times the W4A16 container `packed`."""
+    M, K = X.shape
+    st = lib().w4a16_linear(_dev_ptr(X, 2), _dev_ptr(packed, 1), _dev_ptr(bias, 2), M, N, K, group,
+                            _dev_ptr(Y, 2), _stream(stream))
+    _check("w4a16_linear", st)
 
 
 def svdq_debug_group_partials(qx, qw, P, M, N, K, group=GROUP, qfmt=QFMT_INT4, stream=None):

@@ -33,6 +33,9 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", os.path.join(ROOT, "include"), "-I
 HIP_FLAGS = COMMON + [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
                       "-packed-fp32-ops"]
 CXX_FLAGS = COMMON + ["-I", os.path.join(ROCM, "include"), "-D__HIP_PLATFORM_AMD__", "-pthread"]
+# per-source extras: the W4A16 kernel feeds every MFMA result straight into
+# VALU arithmetic, so its MFMAs write VGPRs (no accumulation-register copies)
+HIP_EXTRA = {"w4a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):
@@ -47,7 +50,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        jobs.append([HIPCC] + HIP_FLAGS + ["-c", src, "-o", obj])
+        jobs.append([HIPCC] + HIP_FLAGS + HIP_EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj])
     for src in sorted(glob.glob(os.path.join(CSRC, "*.cpp"))):
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
         jobs.append([CLANGXX] + CXX_FLAGS + ["-c", src, "-o", obj])

@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int kMaxDevices = 64;
 
 std::mutex g_mutex;
@@ -174,6 +174,18 @@ svdq_status w8a8_prepare_weights(const uint16_t *W, int K, int N, int8_t *qw, fl
     return svdq::w8a8_prepare_impl(W, K, N, qw, sw);
 }
 
+size_t w4a16_weight_bytes(int K, int N) {
+    if (K <= 0 || N <= 0 || K % SVDQ_GROUP) return 0;
+    return svdq::w4a16_container_bytes(K, N);
+}
+
+svdq_status w4a16_prepare_weights(const uint16_t *W, int K, int N, int group, uint8_t *packed) {
+    if (!W || !packed || K <= 0 || N <= 0) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (group != SVDQ_GROUP || K % SVDQ_GROUP) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    if (!svdq::all_finite_bf16(W, (int64_t)K * N)) return SVDQ_ERR_NUMERICAL;
+    return svdq::w4a16_prepare_impl(W, K, N, packed);
+}
+
 // ---------------------------------------------------------------- device ---
 
 svdq_status svdq_channel_absmax(const uint16_t *X, int M, int K, float *absmax, void *stream) {
@@ -263,6 +275,25 @@ svdq_status w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
     if (st != SVDQ_OK) return st;
     if (M == 0) return SVDQ_OK;
     return launched(svdq::launch_w8a8_linear(X, qw, sw, bias, M, N, K, workspace, Y, (hipStream_t)stream));
+}
+
+svdq_status w4a16_linear(const uint16_t *X, const uint8_t *packed, const uint16_t *bias, int M,
+                         int N, int K, int group, uint16_t *Y, void *stream) {
+    if (M < 0 || N <= 0 || K <= 0) return SVDQ_ERR_INVALID_ARGUMENT;
+    // a block keeps at least one row of X and its group sums in LDS
+    if (group != SVDQ_GROUP || K % SVDQ_GROUP || svdq::w4a16_rows_per_block(1, K) < 1)
+        return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    // X and the weight container are read through 32-bit buffer offsets;
+    // blocks are numbered in one grid dimension
+    if (!fits_buffer(M, 2LL * K) || !fits_buffer(1, (int64_t)svdq::w4a16_container_bytes(K, N)) ||
+        ((int64_t)N + 31) / 32 * (((int64_t)M + 15) / 16) >= ((int64_t)1 << 31))
+        return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    if (!packed || (M > 0 && (!X || !Y))) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (!aligned16(X) || !aligned16(packed) || !aligned16(bias) || !aligned16(Y)) return SVDQ_ERR_MISALIGNED;
+    svdq_status st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0) return SVDQ_OK;
+    return launched(svdq::launch_w4a16_linear(X, packed, bias, M, N, K, Y, (hipStream_t)stream));
 }
 
 svdq_status svdq_debug_group_partials(const uint8_t *qx, const uint8_t *qw,

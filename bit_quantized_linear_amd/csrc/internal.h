@@ -20,12 +20,14 @@ svdq_status prepare_residual_impl(const uint16_t *W, int K, int N,
                                   const uint16_t *l2t, int rank, uint8_t *qw,
                                   float *sw);
 svdq_status w8a8_prepare_impl(const uint16_t *W, int K, int N, int8_t *qw, float *sw);
+svdq_status w4a16_prepare_impl(const uint16_t *W, int K, int N, uint8_t *packed);
+size_t w4a16_container_bytes(int K, int N);
 svdq_status repack_codes_impl(const uint8_t *q, int rows, int K, int qfmt, uint8_t *out);
 svdq_status truncated_svd(const double *A, int K, int N, int rank, double *U,
                           double *S, double *V);
 bool all_finite_bf16(const uint16_t *p, int64_t n);
 
-// ---- device launchers (act_quant.hip, w4a4_gemm.hip, w8a8.hip) ----
+// ---- device launchers (act_quant.hip, w4a4_gemm.hip, w4a4_fp6_gemm.hip, w8a8.hip, w4a16.hip) ----
 // Arguments are validated by the caller; launchers only pick a grid and launch.
 hipError_t launch_channel_absmax(const uint16_t *X, int M, int K, float *absmax,
                                  hipStream_t stream);
@@ -53,5 +55,8 @@ hipError_t launch_w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
 hipError_t launch_w8a8_acc(const int8_t *qx, const int8_t *qw, int M, int N,
                            int K, int32_t *acc, hipStream_t stream);
 size_t w8a8_workspace_size(int M, int K);
+int w4a16_rows_per_block(int M, int K);
+hipError_t launch_w4a16_linear(const uint16_t *X, const uint8_t *packed, const uint16_t *bias, int M,
+                               int N, int K, uint16_t *Y, hipStream_t stream);
 
 }  // namespace svdq

@@ -409,6 +409,67 @@ svdq_status w8a8_prepare_impl(const uint16_t *W, int K, int N, int8_t *qw, float
     return SVDQ_OK;
 }
 
+// W4A16 container (the awq_w4a16 layer type): each column's K-groups
+// quantized like the residual above, then written in units of 32 columns
+// (two tiles of 16) x one pair of K-groups (128 k). Unit (b, p) holds 2 x
+// 1024 bytes of codes -- tile j's slot l (16 bytes at 1024 j + 16 l) has, in
+// its dword d, the codes of column 32b + 16j + l % 16 at k = 64(2p + d / 2) +
+// 32(d % 2) + 8(l / 16) + i, i = 0..7, as u = q + 8 with i = 2t at bits 4t
+// and i = 2t + 1 at bits 16 + 4t -- followed by 64 fp32 scales, column
+// 32b + 16j + c and group 2p + e at byte 2048 + 16c + 8j + 4e. Padding
+// (columns past N, the second group of an odd count): u = 8, scale 0.
+size_t w4a16_container_bytes(int K, int N) {
+    const size_t cpairs = (size_t)((N + 31) / 32);
+    const size_t pairs = (size_t)((K / SVDQ_GROUP + 1) / 2);
+    return cpairs * pairs * 2304;
+}
+
+svdq_status w4a16_prepare_impl(const uint16_t *W, int K, int N, uint8_t *packed) {
+    const int G = K / SVDQ_GROUP;
+    const int pairs = (G + 1) / 2;
+    const int cpairs = (N + 31) / 32;
+    std::vector<float> Wf((int64_t)K * N);
+    for (int64_t i = 0; i < (int64_t)K * N; ++i) Wf[i] = bf16_to_f32(W[i]);
+    parallel_for(0, cpairs, [&](int64_t b0, int64_t b1) {
+        std::vector<int8_t> codes((size_t)32 * pairs * 128);  // [column of the pair][k, padded]
+        std::vector<float> scales((size_t)32 * pairs * 2);
+        for (int64_t b = b0; b < b1; ++b) {
+            std::fill(codes.begin(), codes.end(), (int8_t)0);
+            std::fill(scales.begin(), scales.end(), 0.0f);
+            for (int c = 0; c < 32; ++c) {
+                const int64_t n = 32 * b + c;
+                if (n >= N) continue;
+                for (int g = 0; g < G; ++g)
+                    quantize_group_int4(Wf.data() + (int64_t)g * SVDQ_GROUP * N + n, N, SVDQ_GROUP,
+                                        codes.data() + (size_t)c * pairs * 128 + g * SVDQ_GROUP,
+                                        scales.data() + (size_t)c * pairs * 2 + g);
+            }
+            for (int p = 0; p < pairs; ++p) {
+                uint8_t *unit = packed + ((size_t)b * pairs + p) * 2304;
+                for (int j = 0; j < 2; ++j)
+                    for (int l = 0; l < 64; ++l) {
+                        const int c = 16 * j + l % 16;
+                        for (int d = 0; d < 4; ++d) {
+                            const int kb = 64 * (2 * p + d / 2) + 32 * (d % 2) + 8 * (l / 16);
+                            uint32_t w = 0;
+                            for (int i = 0; i < 8; ++i) {
+                                const uint32_t u = (uint32_t)(codes[(size_t)c * pairs * 128 + kb + i] + 8);
+                                w |= u << ((i & 1) ? 16 + 4 * (i / 2) : 4 * (i / 2));
+                            }
+                            std::memcpy(unit + 1024 * j + 16 * l + 4 * d, &w, 4);
+                        }
+                    }
+                for (int c = 0; c < 16; ++c)
+                    for (int j = 0; j < 2; ++j)
+                        for (int e = 0; e < 2; ++e)
+                            std::memcpy(unit + 2048 + 16 * c + 8 * j + 4 * e,
+                                        &scales[(size_t)(16 * j + c) * pairs * 2 + 2 * p + e], 4);
+            }
+        }
+    });
+    return SVDQ_OK;
+}
+
 // Canonical INT4 nibbles -> FP6 container: each code c as FP6 E2M3 of c / 8
 // (sign in bit 5, |c| in bits 0-2); the codes of half h of a group packed
 // LSB-first into 24 bytes H_h; the group's 48 bytes are

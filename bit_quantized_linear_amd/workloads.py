@@ -17,7 +17,7 @@ Every array is drawn in float32 from numpy's PCG64 with a fixed seed, scaled,
 then rounded to bfloat16 (nearest-even on the fp32 bit pattern) and returned
 both as uint16 bit patterns and as the float32 values those bits hold.
 Seeds: X = 1000c, W = 1000c+1, outlier picks = 1000c+2, heavy columns =
-1000c+3, bias = 1000c+4 (c = 1..5, the case number below); the MLP pair's
+1000c+3, bias = 1000c+4 (c = 1..6, the case number below); the MLP pair's
 second weight uses 1000c+5 (values), 1000c+7 (heavy columns) and 1000c+8
 (bias).
 """
@@ -42,7 +42,7 @@ class Case:
     heavy_gain: float
     bias: bool
     rank: int
-    kind: str  # "w4a4", "w8a8"
+    kind: str  # "w4a4", "w8a8", "w4a16"
 
 
 CASES = {
@@ -58,6 +58,9 @@ CASES = {
     # video-scale: 32760 tokens (21 latent frames x 30 x 52 patches), 0.5% (26) x20
     "video": Case("video", 5, 32760, 5120, 5120, 26, 20.0, 0, 1.0, True, 32, "w4a4"),
     "video_w8a8": Case("video_w8a8", 5, 32760, 5120, 5120, 26, 20.0, 0, 1.0, True, 0, "w8a8"),
+    # adaLN modulation of a 3072-wide DiT block (6 x 3072 shift/scale/gate
+    # outputs) on the conditioning vectors of a batch of 2: the W4A16 layer
+    "modulation": Case("modulation", 6, 2, 3072, 18432, 0, 1.0, 0, 1.0, True, 0, "w4a16"),
 }
 
 # the MLP down-projection 12288 -> 3072 takes GELU of the up-projection's

@@ -1,7 +1,8 @@
 /*
  * svdq.h -- C interface of libsvdq.so: the SVDQuant W4A4 linear with its
- * 16-bit low-rank branch, and the INT8 tensorwise W8A8 linear, for AMD
- * Instinct MI355X (gfx950, CDNA4).
+ * 16-bit low-rank branch, the INT8 tensorwise W8A8 linear and the W4A16
+ * linear (4-bit weights, 16-bit activations), for AMD Instinct MI355X
+ * (gfx950, CDNA4).
  *
  * The method (sources, cited by page title and passage):
  *  [HF-SVDQ]   "Hugging Face встроила Nunchaku в Diffusers: диффузия быстрее на
@@ -11,7 +12,9 @@
  *              the hardest part of each weight matrix is a separate 16-bit
  *              low-rank branch; the remainder is quantized to 4 bits.
  *              "Nunchaku Lite" paragraph: such svdq_w4a4 layers replace the
- *              attention and MLP projections (INT4 variant); hardware
+ *              attention and MLP projections (INT4 variant), and awq_w4a16
+ *              layers (4-bit weights, 16-bit activations) the
+ *              precision-sensitive normalization/modulation layers; hardware
  *              paragraph: an unsupported GPU must be refused with a clear
  *              error, never a wrong result.
  *  [KREA-SVDQ] "SVDQuant ускоряет Krea 2 вдвое даже на старых NVIDIA GPU --
@@ -172,6 +175,35 @@ svdq_status svdq_prepare_residual(const uint16_t *W, int K, int N,
 svdq_status w8a8_prepare_weights(const uint16_t *W, int K, int N,
                                  int8_t *qw, float *sw);
 
+/* Bytes of the W4A16 weight container for a [K, N] weight (0 on a bad
+ * argument: K <= 0, N <= 0 or K % 64). */
+size_t w4a16_weight_bytes(int K, int N);
+
+/* W4A16 weight preparation -- the awq_w4a16 layer type [HF-SVDQ "Nunchaku
+ * Lite" paragraph: 4-bit weights with 16-bit activations]. The weight is
+ * quantized with the same INT4 grid as the SVDQuant residual, applied to W
+ * itself (no smoothing, no low-rank branch; AWQ's activation-aware channel
+ * scales, chosen from calibration data, belong to the layer before):
+ *   per output column n and K-group g: A = max |W|, sw = fp32(A / 7),
+ *   q = clamp(round-half-even(fp32(W / sw)), -7, 7); A == 0 -> sw = 0, q = 0.
+ * Out: `packed`, w4a16_weight_bytes(K, N) bytes, laid out for the device
+ * kernel's coalesced stream (the layout is part of the ABI):
+ *  - columns in pairs of 16-column tiles, C = ceil(N / 32) pairs; K in pairs
+ *    of groups, P = ceil(K / 128); unit (b, p) of 2304 bytes at byte
+ *    (b P + p) 2304;
+ *  - unit bytes [1024 j, 1024 j + 1024) hold tile j (j = 0, 1) as 64 slots
+ *    of 16 bytes; dword d (0..3) of slot l holds column n = 32b + 16j +
+ *    l % 16 at k = 64(2p + d / 2) + 32(d % 2) + 8(l / 16) + i, i = 0..7,
+ *    each code as the nibble u = q + 8 (1..15), i = 2t in bits [4t, 4t + 4)
+ *    and i = 2t + 1 in bits [16 + 4t, 20 + 4t);
+ *  - unit bytes [2048, 2304): fp32 sw of column 32b + 16j + c and group
+ *    2p + e at byte 2048 + 16c + 8j + 4e (c = 0..15; j, e = 0..1);
+ *  - columns n >= N and groups g >= K/64 are padding: u = 8, sw = 0.
+ * In: W [K, N] bf16 bits (host), group == 64, K % 64 == 0, N >= 1.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, NUMERICAL (non-finite W). */
+svdq_status w4a16_prepare_weights(const uint16_t *W, int K, int N, int group,
+                                  uint8_t *packed);
+
 /* Re-encodes packed codes from the canonical INT4 container into `qfmt`
  * (SVDQ_QFMT_INT4 copies). In: q [rows, K/2]; out: [rows, svdq_qrow_bytes(K,
  * qfmt)]. Host pointers. Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE (K % 64),
@@ -257,6 +289,26 @@ svdq_status w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
                         const uint16_t *bias, int M, int N, int K,
                         void *workspace, size_t workspace_bytes, uint16_t *Y,
                         void *stream);
+
+/* The W4A16 linear [HF-SVDQ "Nunchaku Lite" paragraph, awq_w4a16]:
+ *   y[m, n] = sum_g sw[g, n] sum_{k in g} X[m, k] q[k, n] + bias[n]
+ *   (bf16 MFMA on the exact bf16 values of X and of the codes, fp32
+ *   accumulation per group, fp32 group scaling), rounded once to bf16
+ *   (round to nearest even).
+ * In:  X [M, K] bf16; packed: the container of w4a16_prepare_weights for
+ *      this K and N; bias [N] bf16 or NULL. group == 64.
+ * Out: Y [M, N] bf16.
+ * Shapes: M >= 0 (M == 0 launches nothing), K % 64 == 0, K <= 28672,
+ *      N >= 1 (any N), M * K < 2^30, w4a16_weight_bytes(K, N) < 2^31. Built
+ *      for the batch sizes of conditioning inputs: the weight is read once
+ *      per block of rows of X (16 rows, fewer once 2 K bytes per row no
+ *      longer fit 56 KB of LDS).
+ * Deterministic (fixed summation order, no atomics).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, MISALIGNED, UNSUPPORTED_DEVICE,
+ *      HIP. */
+svdq_status w4a16_linear(const uint16_t *X, const uint8_t *packed,
+                         const uint16_t *bias, int M, int N, int K, int group,
+                         uint16_t *Y, void *stream);
 
 /* ------------------------------------------- TEST-ONLY (same kernels) --- */
 

@@ -22,21 +22,21 @@ def header_functions():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([a-z_0-9]+)\s*\(", text)
-    keep = [n for n in names if n.startswith(("svdq_", "w8a8_"))]
+    keep = [n for n in names if n.startswith(("svdq_", "w8a8_", "w4a16_"))]
     return sorted(set(keep))
 
 
 def test_every_declared_symbol_is_exported():
     lib = C.CDLL(b.LIB_PATH)
     names = header_functions()
-    assert len(names) >= 14
+    assert len(names) >= 17
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(b.SIGNATURES), "binding and header disagree"
 
 
 def test_status_strings_and_version():
-    assert b.svdq_version() == 3
+    assert b.svdq_version() == 4
     for s in range(7):
         assert b.status_string(s)
     assert "unknown" in b.status_string(99)
@@ -184,3 +184,73 @@ def test_fp6_container_blocks_of_128_rows(rows, K):
     nb = min(128, rows - b0)
     pos = b0 * (K // 4 * 3) + g * nb * 48 + (m - b0) * 48
     assert flat[pos] == 3 and np.count_nonzero(flat) == 1
+
+
+@pytest.mark.parametrize("K,N", [(64, 1), (128, 16), (192, 40), (320, 33), (1024, 96)])
+def test_w4a16_container_matches_the_oracle_and_the_documented_layout(K, N):
+    """Library W4A16 preparation == the oracle's codes and scales written by
+    the test-side writer of the header's layout (bit-exact), including odd
+    group counts and ragged column counts (padding u = 8, scale 0)."""
+    from oracle import w4a16 as o16
+    from tests.w4a16_format import pack_w4a16, unpack_w4a16
+    from bit_quantized_linear_amd import workloads as wl
+
+    rng = np.random.default_rng(K * 7 + N)
+    Wv = (0.02 * rng.standard_normal((K, N))).astype(np.float32)
+    Wv[:, 0] *= 8
+    if N > 2:
+        Wv[64:128, 2] = 0.0  # an all-zero group
+    Wb = wl.bf16_bits_from_f32(Wv)
+    Wf = wl.f32_from_bf16_bits(Wb)
+    qw, sw = o16.prepare_weights(Wf)
+    lib_buf = b.w4a16_prepare_weights(Wb)
+    assert lib_buf.size == b.w4a16_weight_bytes(K, N) == (N + 31) // 32 * ((K // 64 + 1) // 2) * 2304
+    assert np.array_equal(lib_buf, pack_w4a16(qw, sw))
+    q2, s2 = unpack_w4a16(lib_buf, K, N)
+    assert np.array_equal(q2, qw) and np.array_equal(s2, sw)
+
+
+def test_w4a16_one_code_lands_where_the_header_says():
+    from tests.w4a16_format import UNIT
+    from bit_quantized_linear_amd import workloads as wl
+
+    K, N = 256, 72
+    W = np.zeros((K, N), np.float32)
+    # group 3 -> pair p = 1, d = 2 (group 2p + 1, first half) + 1 (second half): d = 3;
+    # column 32 b + 16 j + c with b = 2, j = 0, c = 7; slot l = 16 * 2 + 7 (k slot 2), i = 5
+    k, n = 64 * 3 + 32 + 8 * 2 + 5, 32 * 2 + 7
+    W[k, n] = 1.75  # scale 0.25, code 7 -> u = 15
+    buf = b.w4a16_prepare_weights(wl.bf16_bits_from_f32(W))
+    P = 2
+    unit = buf[(2 * P + 1) * UNIT:(2 * P + 2) * UNIT]
+    word = int(unit[:1024].view(np.uint32)[(16 * 2 + 7) * 4 + 3])
+    assert (word >> (16 + 4 * 2)) & 0xF == 15  # i = 5 -> bits 16 + 4*2
+    assert word & ~(0xF << 24) == 0x88888888 & ~(0xF << 24)
+    assert unit[2048:].view(np.float32)[(16 * 7 + 8 * 0 + 4 * 1) // 4] == 0.25  # c = 7, j = 0, e = 1
+    assert np.count_nonzero(unit[2048:].view(np.float32)) == 1
+
+
+def test_w4a16_shape_and_argument_checks():
+    lib = b.lib()
+    assert b.w4a16_weight_bytes(100, 8) == 0 and b.w4a16_weight_bytes(64, 0) == 0
+    with pytest.raises(b.SvdqError) as e:
+        b.w4a16_prepare_weights(np.zeros((100, 8), np.uint16))
+    assert e.value.status == b.SVDQ_ERR_UNSUPPORTED_SHAPE
+    Wn = np.zeros((64, 8), np.uint16)
+    Wn[1, 1] = 0x7F80  # inf
+    with pytest.raises(b.SvdqError) as e:
+        b.w4a16_prepare_weights(Wn)
+    assert e.value.status == b.SVDQ_ERR_NUMERICAL
+    assert lib.w4a16_linear(FAKE, FAKE, None, 2, 16, 100, 64, FAKE, None) == b.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert lib.w4a16_linear(FAKE, FAKE, None, 2, 16, 128, 32, FAKE, None) == b.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert lib.w4a16_linear(FAKE, FAKE, None, 1, 16, 28736, 64, FAKE, None) == b.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert lib.w4a16_linear(FAKE, None, None, 2, 16, 128, 64, FAKE, None) == b.SVDQ_ERR_INVALID_ARGUMENT
+    assert lib.w4a16_linear(FAKE, FAKE, None, 2, 0, 128, 64, FAKE, None) == b.SVDQ_ERR_INVALID_ARGUMENT
+    assert lib.w4a16_linear(MISALIGNED, FAKE, None, 2, 16, 128, 64, FAKE, None) == b.SVDQ_ERR_MISALIGNED
+    assert lib.w4a16_linear(FAKE, FAKE, None, 1 << 20, 16, 1 << 11, 64, FAKE, None) == \
+        b.SVDQ_ERR_UNSUPPORTED_SHAPE  # M K 2 bytes past 32-bit offsets
+    b.svdq_debug_set_arch_override("gfx942")
+    try:
+        assert lib.w4a16_linear(FAKE, FAKE, None, 2, 16, 128, 64, FAKE, None) == b.SVDQ_ERR_UNSUPPORTED_DEVICE
+    finally:
+        b.svdq_debug_set_arch_override(None)
