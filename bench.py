@@ -17,7 +17,12 @@ over the whole step (both kernels). The roofline object describes the
 dominant kernel (the GEMM) against the dense peak of the MFMA type it runs on
 (FP6); "pct_int8_roofline" gives the same throughput against the int8 MFMA
 peak. The W8A8 linear on the attention shape is timed the same way and
-reported under "w8a8".
+reported under "w8a8". The W4A16 linear (the awq_w4a16 layer type) on an
+adaLN-modulation shape is reported under "w4a16" with its own HBM roofline:
+it is a skinny GEMM whose cost is one read of the packed weight. Its rate is
+taken the way a model runs such layers, one per block with distinct weights:
+a HIP graph of launches round-robin over 16 copies of the weight (twice the
+last-level cache), replayed back to back between two HIP events.
 
 HBM traffic of the GEMM comes from two rocprofv3 counter runs (FETCH_SIZE,
 then WRITE_SIZE) of this script with --calibrate-copy, which adds a plain
@@ -58,6 +63,9 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "svdq_w4a4_linear_fp6_mlp_up_46
 COPY_BYTES = 256 << 20  # calibration kernel: reads and writes this many bytes
 GEMM_KERNEL_KEY = "w4a4_fp6_kernel<true>"
 COPY_KERNEL_KEY = "neg_kernel"
+W16_SOURCES = ("w4a16.hip", "device_common.h")
+W16_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "w4a16_linear_modulation_2x3072x18432_traffic.txt")
+W16_KERNEL_KEY = "w4a16_kernel"
 
 
 def parse():
@@ -68,25 +76,28 @@ def parse():
     p.add_argument("--workload", default="mlp_up")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-w8a8", action="store_true")
+    p.add_argument("--no-w4a16", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=4608,
                    help="token rows of the workload the CPU oracle is timed on")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain elementwise kernel of known size (for counter runs)")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="print the traffic summary from two rocprofv3 --pmc output folders (no GPU)")
+    p.add_argument("--pmc-kernel", choices=("fp6_gemm", "w4a16"), default="fp6_gemm",
+                   help="kernel whose traffic --summarize-pmc reports")
     return p.parse_args()
 
 
-def gemm_source_hash():
+def gemm_source_hash(sources=GEMM_SOURCES):
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in sources:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def _counter_means(folder, counter):
-    """Mean per-dispatch value of `counter` for the GEMM and the calibration kernel."""
+def _counter_means(folder, counter, kernel_key=GEMM_KERNEL_KEY):
+    """Mean per-dispatch value of `counter` for the kernel and the calibration kernel."""
     vals = {"gemm": [], "copy": []}
     for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
@@ -94,7 +105,7 @@ def _counter_means(folder, counter):
                 if r.get("Counter_Name") != counter:
                     continue
                 name = r.get("Kernel_Name", "")
-                key = "gemm" if GEMM_KERNEL_KEY in name else "copy" if COPY_KERNEL_KEY in name else None
+                key = "gemm" if kernel_key in name else "copy" if COPY_KERNEL_KEY in name else None
                 if key:
                     vals[key].append(float(r["Counter_Value"]))
     if not vals["gemm"] or not vals["copy"]:
@@ -102,24 +113,32 @@ def _counter_means(folder, counter):
     return {k: sum(v) / len(v) for k, v in vals.items()}
 
 
-def summarize_pmc(fetch_dir, write_dir):
-    """Text summary of the GEMM's HBM traffic per launch (printed to stdout)."""
-    fe = _counter_means(fetch_dir, "FETCH_SIZE")
-    wr = _counter_means(write_dir, "WRITE_SIZE")
+def summarize_pmc(fetch_dir, write_dir, which="fp6_gemm"):
+    """Text summary of a kernel's HBM traffic per launch (printed to stdout)."""
+    if which == "w4a16":
+        key, sources = W16_KERNEL_KEY, W16_SOURCES
+        M, K, N = 2, 3072, 18432
+        algo = w4a16_bytes(M, K, N)
+        title = f"# HBM traffic of w4a16_linear, modulation M={M} K={K} N={N}"
+    else:
+        key, sources = GEMM_KERNEL_KEY, GEMM_SOURCES
+        M, K, N, r = 4608, 3072, 12288, 32
+        algo = algorithmic_gemm_bytes(M, N, K, r)
+        title = f"# HBM traffic of svdq_w4a4_linear (FP6 container), mlp_up M={M} K={K} N={N} rank={r}"
+    fe = _counter_means(fetch_dir, "FETCH_SIZE", key)
+    wr = _counter_means(write_dir, "WRITE_SIZE", key)
     # the calibration kernel moves COPY_BYTES each way: counter units -> bytes
     f_scale = COPY_BYTES / fe["copy"]
     w_scale = COPY_BYTES / wr["copy"]
     fetch_b = fe["gemm"] * f_scale
     write_b = wr["gemm"] * w_scale
-    M, K, N, r = 4608, 3072, 12288, 32
-    algo = algorithmic_gemm_bytes(M, N, K, r)
     lines = [
-        "# HBM traffic of svdq_w4a4_linear (FP6 container), mlp_up M=4608 K=3072 N=12288 rank=32",
-        f"kernel_source_sha256_16: {gemm_source_hash()}",
+        title,
+        f"kernel_source_sha256_16: {gemm_source_hash(sources)}",
         f"calibration: elementwise negation of {COPY_BYTES} bytes (reads and writes that many)",
-        f"FETCH_SIZE gemm mean per dispatch (counter units): {fe['gemm']:.1f}",
+        f"FETCH_SIZE kernel mean per dispatch (counter units): {fe['gemm']:.1f}",
         f"FETCH_SIZE calibration kernel (counter units): {fe['copy']:.1f}  -> {f_scale:.2f} bytes/unit",
-        f"WRITE_SIZE gemm mean per dispatch (counter units): {wr['gemm']:.1f}",
+        f"WRITE_SIZE kernel mean per dispatch (counter units): {wr['gemm']:.1f}",
         f"WRITE_SIZE calibration kernel (counter units): {wr['copy']:.1f}  -> {w_scale:.2f} bytes/unit",
         f"fetch_bytes_per_launch: {fetch_b:.0f}",
         f"write_bytes_per_launch: {write_b:.0f}",
@@ -130,22 +149,30 @@ def summarize_pmc(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
-def read_traffic_summary():
-    """(traffic bytes per launch, details) from the committed summary, or
-    (None, reason) when it is missing or the GEMM sources changed since."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+def w4a16_bytes(M, K, N):
+    """Bytes the W4A16 linear must move at least once: the packed weight
+    container (codes and scales, padded to whole 32-column units), bf16 X,
+    bias and Y."""
+    cpairs, pairs = (N + 31) // 32, (K // 64 + 1) // 2
+    return cpairs * pairs * 2304 + M * K * 2 + N * 2 + M * N * 2
+
+
+def read_traffic_summary(path=TRAFFIC_SUMMARY, sources=GEMM_SOURCES):
+    """(traffic bytes per launch, details) from a committed summary, or
+    (None, reason) when it is missing or the kernel's sources changed since."""
+    if not os.path.exists(path):
         return None, "no counter summary"
     kv = {}
-    with open(TRAFFIC_SUMMARY) as fh:
+    with open(path) as fh:
         for line in fh:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != gemm_source_hash():
+    if kv.get("kernel_source_sha256_16") != gemm_source_hash(sources):
         return None, "kernel changed since the counters were taken"
     return float(kv["traffic_bytes_per_launch"]), {
         "fetch_bytes": float(kv["fetch_bytes_per_launch"]), "write_bytes": float(kv["write_bytes_per_launch"]),
-        "source": os.path.relpath(TRAFFIC_SUMMARY, ROOT)}
+        "source": os.path.relpath(path, ROOT)}
 
 
 def algorithmic_gemm_bytes(M, N, K, r):
@@ -269,10 +296,52 @@ def cpu_baseline_w8a8(case, X, W, bias):
             "sample": f"oracle W8A8 forward on the whole workload M={case.M} K={case.K} N={case.N}"}
 
 
+def time_cold_read_flush(fn, reps):
+    """Per-launch ms of `fn` with the caches flushed by reading 1 GiB right
+    before (no synchronize in between: the read keeps the stream busy while
+    the events and the launch are enqueued)."""
+    import torch
+
+    big = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    out = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        big.sum()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    del big
+    return out
+
+
+def cpu_baseline_w4a16(case, X, W, bias):
+    """The W4A16 oracle, untuned, on the whole workload (quantize W, dequantize,
+    fp64 product, bias, bf16), the forward repeated until about 3 s."""
+    from oracle import w4a16 as o16
+
+    qw, sw = o16.prepare_weights(W["values"])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        o16.forward(X["values"], qw, sw, bias["values"])
+        reps += 1
+        if time.perf_counter() - t0 >= 3.0 or reps == 20:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    nbytes = case.K * case.N // 2 + case.K // 64 * case.N * 4
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s of packed weight", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle", "seconds": dt, "passes": reps,
+            "sample": f"oracle W4A16 forward (dequantize + fp64 matmul + bias + bf16) on the whole workload "
+                      f"M={case.M} K={case.K} N={case.N}"}
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
+        summarize_pmc(*args.summarize_pmc, which=args.pmc_kernel)
         return
     if args.gpus != 1:
         print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on one GPU only "
@@ -423,6 +492,76 @@ def main():
         if not args.no_cpu_baseline:
             out["w8a8"]["cpu_baseline"] = cpu_baseline_w8a8(c8, X8, W8, b8)
             log(f"[bench] w8a8 cpu baseline {out['w8a8']['cpu_baseline']['seconds']:.1f}s")
+
+    if not args.no_w4a16:
+        c16 = wl.CASES["modulation"]
+        X16 = wl.activations(c16)
+        W16 = wl.weight(c16)
+        b16 = wl.bias(c16)
+        t1 = time.perf_counter()
+        packed16 = b.w4a16_prepare_weights(W16["bits"])
+        prep16_s = time.perf_counter() - t1
+        X16d, p16d, b16d = up(X16["bits"]), up(packed16), up(b16["bits"])
+        Y16 = torch.empty((c16.M, c16.N), dtype=torch.int16, device="cuda")
+
+        def w16():
+            b.w4a16_linear(X16d, p16d, b16d, Y16, c16.N)
+
+        ms16, _, _, _ = time_steps([w16], max(args.steps, 100), args.warmup)
+        cold16 = time_cold_read_flush(w16, 30)
+        cold_ms = float(np.median(cold16))
+        # HBM-streaming rate: a model has one such layer per block, each with
+        # its own weights, so the layer is launched round-robin over 16 copies
+        # of the container (512 MB, twice the last-level cache): every launch
+        # reads its weights from HBM. The launches are captured once in a HIP
+        # graph and replayed back to back; HIP events around each replay on
+        # the replay stream give the average launch duration.
+        copies = [p16d.clone() for _ in range(16)]
+        rounds = 2
+        gstream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=gstream):
+            for _ in range(rounds):
+                for cp in copies:
+                    b.w4a16_linear(X16d, cp, b16d, Y16, c16.N)
+        graph.replay()
+        torch.cuda.synchronize()
+        rr = []
+        with torch.cuda.stream(gstream):
+            for _ in range(20):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(gstream)
+                graph.replay()
+                e1.record(gstream)
+                gstream.synchronize()
+                rr.append(e0.elapsed_time(e1) / (rounds * len(copies)))
+        hbm_ms = float(np.median(rr))
+        del graph, copies
+        bytes16 = w4a16_bytes(c16.M, c16.K, c16.N)
+        assert bytes16 == packed16.size + c16.M * c16.K * 2 + c16.M * c16.N * 2 + c16.N * 2
+        traffic16, traffic16_detail = read_traffic_summary(W16_TRAFFIC_SUMMARY, W16_SOURCES)
+        gbs = bytes16 / (hbm_ms * 1e-3) / 1e9
+        out["w4a16"] = {
+            "workload": f"{c16.name}: W4A16 linear M={c16.M} K={c16.K} N={c16.N} group=64 "
+                        "(adaLN modulation: 6 x 3072 outputs of a batch of 2 conditioning vectors)",
+            "ms_per_launch": round(hbm_ms, 5),
+            "ms_single_layer_back_to_back_events": round(ms16, 5),
+            "ms_single_layer_cold_events_median": round(cold_ms, 5),
+            "roofline": {"bound": "hbm", "kernel": "w4a16_linear", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "timing": "HIP graph of 32 launches round-robin over 16 weight copies (512 MB), "
+                                   "events around each replay, median of 20 replays",
+                         "algorithmic_bytes": bytes16, "traffic": traffic16,
+                         "traffic_detail": traffic16_detail},
+            "prepare_library_s": round(prep16_s, 3),
+        }
+        log(f"[bench] w4a16 {hbm_ms * 1e3:.2f} us per launch from HBM ({gbs:.0f} GB/s); single layer: "
+            f"back to back {ms16 * 1e3:.2f} us, cold {cold_ms * 1e3:.2f} us (events, incl. launch gaps)")
+        if not args.no_cpu_baseline:
+            out["w4a16"]["cpu_baseline"] = cpu_baseline_w4a16(c16, X16, W16, b16)
+            log(f"[bench] w4a16 cpu baseline {out['w4a16']['cpu_baseline']['seconds']:.3f}s")
 
     out["prepare"] = {"library_s": round(prep_s, 3),
                       "what": "svdq_prepare_weights on the host: smoothing, rank-r SVD, bf16 factors, "

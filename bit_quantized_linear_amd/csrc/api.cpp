@@ -286,7 +286,7 @@ svdq_status w4a16_linear(const uint16_t *X, const uint8_t *packed, const uint16_
     // X and the weight container are read through 32-bit buffer offsets;
     // blocks are numbered in one grid dimension
     if (!fits_buffer(M, 2LL * K) || !fits_buffer(1, (int64_t)svdq::w4a16_container_bytes(K, N)) ||
-        ((int64_t)N + 31) / 32 * (((int64_t)M + 15) / 16) >= ((int64_t)1 << 31))
+        2 * (((int64_t)N + 31) / 32) * (int64_t)M >= ((int64_t)1 << 31))
         return SVDQ_ERR_UNSUPPORTED_SHAPE;
     if (!packed || (M > 0 && (!X || !Y))) return SVDQ_ERR_INVALID_ARGUMENT;
     if (!aligned16(X) || !aligned16(packed) || !aligned16(bias) || !aligned16(Y)) return SVDQ_ERR_MISALIGNED;

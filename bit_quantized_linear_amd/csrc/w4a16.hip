@@ -36,9 +36,13 @@ constexpr uint32_t kW16LdsMax = 56u << 10;  // dynamic LDS of a block: its rows 
 
 typedef __attribute__((address_space(3))) void w16_lds_void;
 
+// One unit in registers: the lane's 16 code bytes of each of the NT tiles
+// the block computes, and the 4 scales of column lane % 16: (tile 0,
+// tile 1) x (group 2p, 2p + 1).
+template <int NT>
 struct W16Unit {
-    u32x4 code[2];  // lane's 16 code bytes of tile 0 and tile 1
-    u32x4 scale;    // column lane % 16: (tile 0, tile 1) x (group 2p, 2p + 1)
+    u32x4 code[NT];
+    u32x4 scale;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t w16_rsrc(const void *p, uint32_t bytes) {
@@ -66,10 +70,13 @@ __device__ __forceinline__ bf16x8 w16_decode(uint32_t w, uint32_t mask_s, uint32
 
 // Loads of one unit: codes and scales through buffer loads whose per-lane
 // offsets are fixed (the unit offset rides in soffset) ...
-__device__ __forceinline__ void w16_load_w(W16Unit &r, __amdgpu_buffer_rsrc_t rw, uint32_t unit,
-                                           uint32_t lane16, uint32_t scale_off) {
-    r.code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, lane16, unit, 0));
-    r.code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, lane16 + 1024u, unit, 0));
+template <int NT>
+__device__ __forceinline__ void w16_load_w(W16Unit<NT> &r, __amdgpu_buffer_rsrc_t rw, uint32_t unit,
+                                           uint32_t code_off, uint32_t scale_off) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+        r.code[j] = __builtin_bit_cast(u32x4,
+                                       __builtin_amdgcn_raw_buffer_load_b128(rw, code_off + 1024u * j, unit, 0));
     r.scale = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, scale_off, unit, 0));
 }
 
@@ -84,11 +91,12 @@ __device__ __forceinline__ void w16_load_x(u32x4 x[4], const uint8_t *xs, const 
 }
 
 // acc[j] += sw[j, g] * (sum_{k in g} x (136 + q) - 136 sum_{k in g} x) for
-// the two groups g of the unit and its two tiles j: the -136 S term comes
-// from MFMAs against a B operand of -136 (x * 136 is exact in fp32) and
-// seeds both tiles' accumulations.
-__device__ __forceinline__ void w16_compute(const W16Unit &r, const u32x4 x[4], f32x4 acc[2],
-                                            uint32_t mask_s, uint32_t magic_v) {
+// the two groups g of the unit and its NT tiles j (tile j0 + j of the
+// unit): the -136 S term comes from MFMAs against a B operand of -136
+// (x * 136 is exact in fp32) and seeds the tiles' accumulations.
+template <int NT>
+__device__ __forceinline__ void w16_compute(const W16Unit<NT> &r, const u32x4 x[4], f32x4 acc[NT],
+                                            uint32_t mask_s, uint32_t magic_v, int j0) {
     const bf16x8 neg136 = __builtin_bit_cast(bf16x8, u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -97,38 +105,44 @@ __device__ __forceinline__ void w16_compute(const W16Unit &r, const u32x4 x[4], 
         f32x4 c = mfma_bf16_16x16x32(a0, neg136, f32x4{0.f, 0.f, 0.f, 0.f});
         c = mfma_bf16_16x16x32(a1, neg136, c);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NT; ++j) {
             f32x4 d = mfma_bf16_16x16x32(a0, w16_decode(r.code[j][2 * e], mask_s, magic_v), c);
             d = mfma_bf16_16x16x32(a1, w16_decode(r.code[j][2 * e + 1], mask_s, magic_v), d);
-            const float sc = __uint_as_float(r.scale[2 * j + e]);
+            const uint32_t sbits = NT == 2 ? r.scale[2 * j + e] : (j0 ? r.scale[2 + e] : r.scale[e]);
+            const float sc = __uint_as_float(sbits);
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_fmaf(sc, d[i], acc[j][i]);
         }
     }
 }
 
-// One block: 32 output columns x `rows` batch rows (rows <= 16); its
-// kW16Waves waves take the K pairs w, w + kW16Waves, ... and add their
-// partial sums in LDS. Dynamic LDS: the block's rows of X ([rows][K] bf16,
+// One block: 16 NT output columns (both tiles of a unit, or tile j0 of it)
+// x `rows` batch rows (rows <= 16); its kW16Waves waves take the K pairs
+// w, w + kW16Waves, ... and add their partial sums in LDS. Blocks of one
+// tile each double the block count of a skinny layer, which spreads its
+// work more evenly over the compute units; two tiles per block share the
+// A fragments, which pays once the batch fills the MFMA rows. Dynamic LDS: the block's rows of X ([rows][K] bf16,
 // padded to whole KB). MFMA rows past the block's rows read the last row's
 // X and are never stored (each output row depends on its own A row only).
-template <int kW16Waves>
+template <int kW16Waves, int NT>
 __global__ __launch_bounds__(64 * kW16Waves) void w4a16_kernel(
     const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed,
     const uint16_t *__restrict__ bias, int M, int N, int K, int P, int units, int rows, int m_chunks,
     uint32_t x_lds_bytes, uint32_t mask_s, uint32_t magic_s, uint16_t *__restrict__ Y) {
     extern __shared__ __align__(16) uint8_t xs[];
-    __shared__ f32x4 red[kW16Waves][2][64];
+    __shared__ f32x4 red[kW16Waves][NT][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
     // blocks of one column pair are adjacent, so the batch chunks of a pair
     // read its weights while they are in L2
-    const int cpair = (int)(blockIdx.x / (unsigned)m_chunks);
+    const int tb = (int)(blockIdx.x / (unsigned)m_chunks);
+    const int cpair = NT == 2 ? tb : tb >> 1;
+    const int j0 = NT == 2 ? 0 : (tb & 1);
     const int m0 = (int)(blockIdx.x % (unsigned)m_chunks) * rows;
     const int rows_here = min(rows, M - m0);
 
     const __amdgpu_buffer_rsrc_t rw = w16_rsrc(packed, (uint32_t)units * kW16Unit);
-    const uint32_t lane16 = 16u * (uint32_t)lane;
+    const uint32_t code_off = 16u * (uint32_t)lane + 1024u * (uint32_t)j0;
     const uint32_t scale_off = 2048u + 16u * (uint32_t)(lane & 15);
     const uint32_t unit0 = (uint32_t)cpair * (uint32_t)P * kW16Unit;
     const int xrow = min(lane & 15, rows_here - 1);
@@ -148,9 +162,11 @@ __global__ __launch_bounds__(64 * kW16Waves) void w4a16_kernel(
         }
     };
 
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int n_iter = wave < P ? (P - wave + kW16Waves - 1) / kW16Waves : 0;
-    W16Unit buf[kW16Depth];
+    W16Unit<NT> buf[kW16Depth];
 
     // X rows m0 .. m0 + rows_here - 1 -> LDS, 1 KB per wave instruction
     // (past the end of X the range check returns zeros), issued together
@@ -168,18 +184,18 @@ __global__ __launch_bounds__(64 * kW16Waves) void w4a16_kernel(
 #pragma unroll
     for (int d = 0; d < kW16Depth; ++d) {
         const int p = min(wave + kW16Waves * d, P - 1);
-        w16_load_w(buf[d], rw, unit0 + (uint32_t)p * kW16Unit, lane16, scale_off);
+        w16_load_w<NT>(buf[d], rw, unit0 + (uint32_t)p * kW16Unit, code_off, scale_off);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the copy of X in LDS
     __builtin_amdgcn_s_barrier();
     // unit it of this wave: weights from the ring, A fragments from LDS
     // (read just before use: LDS latency is short)
-    auto step = [&](const W16Unit &u, int it) {
+    auto step = [&](const W16Unit<NT> &u, int it) {
         uint32_t xoff[2];
         x_offsets(wave + kW16Waves * it, xoff);
         u32x4 x[4];
         w16_load_x(x, xs, xoff);
-        w16_compute(u, x, acc, mask_s, magic_v);
+        w16_compute<NT>(u, x, acc, mask_s, magic_v, j0);
     };
     // full rounds: straight-line code, so the loads of the next round stay in
     // flight while this round computes
@@ -189,20 +205,20 @@ __global__ __launch_bounds__(64 * kW16Waves) void w4a16_kernel(
         for (int d = 0; d < kW16Depth; ++d) {
             step(buf[d], it + d);
             const int p = min(wave + kW16Waves * (it + d + kW16Depth), P - 1);
-            w16_load_w(buf[d], rw, unit0 + (uint32_t)p * kW16Unit, lane16, scale_off);
+            w16_load_w<NT>(buf[d], rw, unit0 + (uint32_t)p * kW16Unit, code_off, scale_off);
         }
     }
 #pragma unroll
     for (int d = 0; d < kW16Depth - 1; ++d)
         if (it + d < n_iter) step(buf[d], it + d);
 
-    red[wave][0][lane] = acc[0];
-    red[wave][1][lane] = acc[1];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) red[wave][j][lane] = acc[j];
     __syncthreads();
-    // 2 tiles x 16 rows x 16 columns; consecutive threads take consecutive
+    // NT tiles x 16 rows x 16 columns; consecutive threads take consecutive
     // columns of one output row
 #pragma unroll
-    for (int idx = threadIdx.x; idx < 512; idx += 64 * kW16Waves) {
+    for (int idx = threadIdx.x; idx < 256 * NT; idx += 64 * kW16Waves) {
         const int j = idx >> 8;
         const int r = (idx >> 4) & 15;
         const int c = idx & 15;
@@ -210,7 +226,7 @@ __global__ __launch_bounds__(64 * kW16Waves) void w4a16_kernel(
         float v = 0.0f;
 #pragma unroll
         for (int w = 0; w < kW16Waves; ++w) v += red[w][j][src][r & 3];
-        const int n = 32 * cpair + 16 * j + c;
+        const int n = 32 * cpair + 16 * (j0 + j) + c;
         if (r < rows_here && n < N) {
             if (bias) v += bf16_bits_to_f32(bias[n]);
             Y[(size_t)(m0 + r) * N + n] = (uint16_t)f32_to_bf16_bits(v);
@@ -238,15 +254,23 @@ hipError_t launch_w4a16_linear(const uint16_t *X, const uint8_t *packed, const u
     const int rows = w4a16_rows_per_block(M, K);
     const int m_chunks = (M + rows - 1) / rows;
     const int cpairs = (N + 31) / 32;
-    const int64_t blocks = (int64_t)cpairs * m_chunks;
     const uint32_t xb = x_lds_bytes(rows, K);
-    // fewer blocks than compute units: split K over more waves per block
-    if (blocks < 256 && P >= 16)
-        hipLaunchKernelGGL(w4a16_kernel<8>, dim3((unsigned)blocks), dim3(512), xb, stream, X, packed, bias,
-                           M, N, K, P, cpairs * P, rows, m_chunks, xb, 0x000F000Fu, 0x43004300u, Y);
-    else
-        hipLaunchKernelGGL(w4a16_kernel<4>, dim3((unsigned)blocks), dim3(256), xb, stream, X, packed, bias,
-                           M, N, K, P, cpairs * P, rows, m_chunks, xb, 0x000F000Fu, 0x43004300u, Y);
+    const int units = cpairs * P;
+    if (rows <= 8) {
+        // a skinny batch: one 16-column tile per block
+        const unsigned blocks = (unsigned)((int64_t)2 * cpairs * m_chunks);
+        hipLaunchKernelGGL((w4a16_kernel<4, 1>), dim3(blocks), dim3(256), xb, stream, X, packed, bias, M, N, K, P,
+                           units, rows, m_chunks, xb, 0x000F000Fu, 0x43004300u, Y);
+    } else {
+        const int64_t blocks = (int64_t)cpairs * m_chunks;
+        // fewer blocks than compute units: split K over more waves per block
+        if (blocks < 256 && P >= 16)
+            hipLaunchKernelGGL((w4a16_kernel<8, 2>), dim3((unsigned)blocks), dim3(512), xb, stream, X, packed,
+                               bias, M, N, K, P, units, rows, m_chunks, xb, 0x000F000Fu, 0x43004300u, Y);
+        else
+            hipLaunchKernelGGL((w4a16_kernel<4, 2>), dim3((unsigned)blocks), dim3(256), xb, stream, X, packed,
+                               bias, M, N, K, P, units, rows, m_chunks, xb, 0x000F000Fu, 0x43004300u, Y);
+    }
     return hipGetLastError();
 }
 
