@@ -91,8 +91,10 @@ def problem(M, K, N, seed, bias=True, outliers=0):
     (1, 64, 16), (2, 64, 1), (2, 192, 40), (3, 320, 100), (5, 128, 33),
     (16, 1024, 96), (17, 512, 64), (33, 256, 72), (2, 3072, 544), (1, 4096, 1000),
     # rows of X per block limited by LDS: 2 (K = 12288, 3 chunks), 1 (K = 28672);
-    # few column pairs at large K (more waves per block)
-    (5, 12288, 64), (3, 14336, 40), (2, 28672, 48), (2, 12288, 3072),
+    # few column pairs at large K; an odd group count at large K
+    (5, 12288, 64), (3, 14336, 40), (2, 28672, 48), (2, 12288, 3072), (2, 12224, 80),
+    # more than 8 rows per block: two tiles per block (and 8 waves with few blocks)
+    (40, 3072, 1024), (12, 4096, 256),
 ])
 def test_w4a16_matches_oracle(M, K, N):
     say(f"w4a16 M={M} K={K} N={N}")
