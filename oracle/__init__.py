@@ -25,11 +25,13 @@ against the pages:
   the "Compiler" bullet listing the ``int4-group`` physical format.
 * [HF-SVDQ] "Nunchaku Lite" paragraph, second layer type: awq_w4a16, 4-bit
   weights with 16-bit activations for normalization/modulation layers
-  (``oracle/w4a16.py``).
+  (``oracle/w4a16.py``); and the 4-bit float variant of svdq_w4a4, built as
+  OCP MXFP4 (``oracle/mxfp4.py``).
 
 Where the pages leave a step open, the reading taken is stated at the
 function that takes it. Parity status of every function is listed in
-``oracle/svdquant.py``, ``oracle/w8a8.py`` and ``oracle/w4a16.py`` headers.
+``oracle/svdquant.py``, ``oracle/w8a8.py``, ``oracle/w4a16.py`` and
+``oracle/mxfp4.py`` headers.
 """
 
-from . import svdquant, w4a16, w8a8  # noqa: F401
+from . import mxfp4, svdquant, w4a16, w8a8  # noqa: F401

@@ -212,3 +212,87 @@ def w4a16_forward(X, W, bias, group=64):
             row.append(bf16_exact(acc))
         y.append(row)
     return qw, sw, y
+
+
+# ---- MXFP4 (OCP microscaling, FP4 E2M1 elements, E8M0 block scales) ----
+
+_E2M1 = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+         Fraction(4), Fraction(6)]
+
+
+def e2m1_code(v: Fraction) -> int:
+    """Nearest E2M1 value of an exact rational, ties to the even mantissa
+    (codes 0, 2, 4, 6 have mantissa 0), magnitudes beyond 6 -> 6, zero -> +0."""
+    m = abs(Fraction(v))
+    best = None
+    for c, g in enumerate(_E2M1):
+        d = abs(m - g)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    c = best[1]
+    if c == 0:
+        return 0
+    return c + (8 if v < 0 else 0)
+
+
+def e2m1_value(code: int) -> Fraction:
+    return -_E2M1[code & 7] if code & 8 else _E2M1[code & 7]
+
+
+def mx_block(values):
+    """One MX block: e with 2^(e+2) <= amax < 2^(e+3) (found by exact
+    comparison), clamped to [-127, 127], -127 for an all-zero block; codes of
+    v / 2^e. Returns (codes, e)."""
+    amax = max(abs(Fraction(v)) for v in values)
+    if amax == 0:
+        return [0] * len(values), -127
+    e = 0
+    while Fraction(2) ** (e + 2) > amax:
+        e -= 1
+    while Fraction(2) ** (e + 3) <= amax:
+        e += 1
+    e = max(-127, min(127, e))
+    return [e2m1_code(Fraction(v) / Fraction(2) ** e) for v in values], e
+
+
+def mx_forward(Xh, R, T, L2, bias, block=32, out="bf16"):
+    """MXFP4 main product plus low-rank and bias, element by element.
+    Xh [M][K] smoothed activations (fp32 values), R [K][N] residual (fp32
+    values), T [M][r], L2 [r][N]. Returns (qx, ex, qw [N][K], ew [N][K/B], y)."""
+    M, K = len(Xh), len(Xh[0])
+    N = len(R[0])
+    r = len(L2)
+    qx, ex = [], []
+    for m in range(M):
+        codes, es = [], []
+        for b in range(K // block):
+            c, e = mx_block(Xh[m][b * block:(b + 1) * block])
+            codes += c
+            es.append(e)
+        qx.append(codes)
+        ex.append(es)
+    qw, ew = [], []
+    for n in range(N):
+        codes, es = [], []
+        for b in range(K // block):
+            c, e = mx_block([R[k][n] for k in range(b * block, (b + 1) * block)])
+            codes += c
+            es.append(e)
+        qw.append(codes)
+        ew.append(es)
+    y = []
+    for m in range(M):
+        row = []
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                b = k // block
+                acc += (e2m1_value(qx[m][k]) * Fraction(2) ** ex[m][b]) * \
+                       (e2m1_value(qw[n][k]) * Fraction(2) ** ew[n][b])
+            for j in range(r):
+                acc += Fraction(T[m][j]) * Fraction(L2[j][n])
+            if bias is not None:
+                acc += Fraction(bias[n])
+            row.append(rn32_exact(acc) if out == "f32" else bf16_exact(acc))
+        y.append(row)
+    return qx, ex, qw, ew, y
