@@ -46,6 +46,10 @@ SIGNATURES = {
     "svdq_w4a4_linear": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
     "w8a8_workspace_bytes": (_sz, [_i, _i]),
     "w8a8_linear": (_i, [_vp, _vp, _f, _vp, _i, _i, _i, _vp, _sz, _vp, _vp]),
+    "svdq_mx_scale_ld": (_sz, [_i]),
+    "svdq_mx_prepare_residual": (_i, [_vp, _i, _i, _vp, _vp, _vp, _i, _vp, _vp]),
+    "svdq_mx_quantize_act": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "svdq_mx_linear": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _vp]),
     "w4a16_weight_bytes": (_sz, [_i, _i]),
     "w4a16_prepare_weights": (_i, [_vp, _i, _i, _i, _vp]),
     "w4a16_linear": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
@@ -198,6 +202,29 @@ def w8a8_prepare_weights(W_bits):
     return qw, float(sw[0])
 
 
+def svdq_mx_scale_ld(rows) -> int:
+    """Row stride (bytes) of an MXFP4 scale matrix [K/32, ld] for `rows` rows."""
+    return int(lib().svdq_mx_scale_ld(rows))
+
+
+def svdq_mx_prepare_residual(W_bits, smooth, l1t, l2t):
+    """MXFP4 residual of a bf16 weight W [K, N] given smoothing and factors:
+    codes (MX container, N rows of K/2 bytes) and E8M0 scales [K/32, ld(N)]."""
+    W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    smooth = np.ascontiguousarray(smooth, dtype=np.float32)
+    l1t = np.ascontiguousarray(l1t, dtype=np.uint16)
+    l2t = np.ascontiguousarray(l2t, dtype=np.uint16)
+    K, N = W_bits.shape
+    rank = l1t.shape[0]
+    qw = np.empty((N, K // 2), np.uint8)
+    uw = np.zeros((max(K // 32, 0), svdq_mx_scale_ld(N)), np.uint8)
+    st = lib().svdq_mx_prepare_residual(_np_ptr(W_bits, np.uint16), K, N, _np_ptr(smooth, np.float32),
+                                        l1t.ctypes.data if rank else None, l2t.ctypes.data if rank else None,
+                                        rank, qw.ctypes.data, uw.ctypes.data)
+    _check("svdq_mx_prepare_residual", st)
+    return {"qw": qw, "uw": uw}
+
+
 def w4a16_weight_bytes(K, N) -> int:
     return int(lib().w4a16_weight_bytes(K, N))
 
@@ -250,6 +277,21 @@ def w8a8_linear(X, qw, sw, bias, workspace, Y, stream=None):
                            _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
                            _dev_ptr(Y, 2), _stream(stream))
     _check("w8a8_linear", st)
+
+
+def svdq_mx_quantize_act(X, smooth, l1t, qx, ux, T, rank, stream=None):
+    M, K = X.shape
+    st = lib().svdq_mx_quantize_act(_dev_ptr(X, 2), _dev_ptr(smooth, 4), _dev_ptr(l1t, 2), M, K, rank,
+                                    _dev_ptr(qx, 1), _dev_ptr(ux, 1), _dev_ptr(T, 2), _stream(stream))
+    _check("svdq_mx_quantize_act", st)
+
+
+def svdq_mx_linear(qx, ux, T, qw, uw, l2t, bias, Y, M, N, K, rank, stream=None):
+    y_dtype = SVDQ_F32 if Y.element_size() == 4 else SVDQ_BF16
+    st = lib().svdq_mx_linear(_dev_ptr(qx, 1), _dev_ptr(ux, 1), _dev_ptr(T, 2), _dev_ptr(qw, 1), _dev_ptr(uw, 1),
+                              _dev_ptr(l2t, 2), _dev_ptr(bias, 2), M, N, K, rank, _dev_ptr(Y), y_dtype,
+                              _stream(stream))
+    _check("svdq_mx_linear", st)
 
 
 def w4a16_linear(X, packed, bias, Y, N, group=GROUP, stream=None):

@@ -44,11 +44,36 @@ __device__ __forceinline__ float quotient_fp32(float a, double r) {
     return (float)((double)a * r);
 }
 
-template <bool kFp6, int RT>
+// E2M1 code of q (|q| < 8): nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to
+// the even mantissa (rintf rounds half to even, and in each binade the even
+// multiple of the quantum is the even mantissa), saturating at 6; bit 3 is
+// the sign; a value that rounds to zero is +0.
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+    const float m = fabsf(q);
+    const float r = m < 2.0f ? rintf(2.0f * m) * 0.5f : (m < 4.0f ? rintf(m) : fminf(6.0f, 2.0f * rintf(0.5f * m)));
+    const int c = r < 2.0f ? (int)(2.0f * r) : (r < 4.0f ? (int)r + 2 : (int)(0.5f * r) + 4);
+    return (uint32_t)c | ((c != 0 && q < 0.0f) ? 8u : 0u);
+}
+
+// MX shared exponent of a block: floor(log2 amax) - 2 clamped to [-127, 127],
+// -127 for amax == 0, read off the fp32 bit pattern.
+__device__ __forceinline__ int mx_exponent(float amax) {
+    const uint32_t b = __float_as_uint(amax);
+    if (b == 0u) return -127;
+    const int ex = (int)(b >> 23);
+    const int fl = ex != 0 ? ex - 127 : (31 - __clz((int)b)) - 149;  // floor(log2 amax), subnormals too
+    return min(127, max(-127, fl - 2));
+}
+
+enum ActFmt { kInt4 = 0, kFp6 = 1, kMx = 2 };
+
+// kFmt: kInt4 / kFp6 write INT4 codes with fp32 group scales (sx [K/64, M]);
+// kMx writes MXFP4 codes with E8M0 block scales (sx points to u8 [K/32][ld]).
+template <int kFmt, int RT>
 __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ smooth,
     const uint16_t *__restrict__ l1t, int M, int K, int rank,
-    uint8_t *__restrict__ qx, float *__restrict__ sx, uint16_t *__restrict__ T) {
+    uint8_t *__restrict__ qx, void *__restrict__ sx_out, int sx_ld, uint16_t *__restrict__ T) {
     constexpr int kRT = RT > 0 ? RT : 1;  // rank tiles held (rank / 16, at least one array slot)
     __shared__ float red[kActWaves][kActRows][16 * kRT];
     __shared__ double rcp[kActWaves][SVDQ_GROUP];  // per wave: 1/s of its current group's channels
@@ -108,11 +133,13 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
 #pragma unroll
         for (int t = 0; t < 16; ++t) xh[t] = quotient_fp32(xb16[t], rq[t]);
         __builtin_amdgcn_wave_barrier();
-        float amax = 0.0f;
+        // bamax: the 32-channel half of the group (lanes of quads 0-1 or 2-3),
+        // amax: the whole group
+        float bamax = 0.0f;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(xh[t]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        for (int t = 0; t < 16; ++t) bamax = fmaxf(bamax, fabsf(xh[t]));
+        bamax = fmaxf(bamax, __shfl_xor(bamax, 16));
+        float amax = fmaxf(bamax, __shfl_xor(bamax, 32));
         if (amax < kTinyGroup) {
             // below the range quotient_fp32 covers: plain IEEE divisions
             // (all four lanes of the row take this branch together)
@@ -123,16 +150,35 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
 #pragma unroll
                 for (int t = 0; t < 4; ++t) xh[4 * i + t] = xb16[4 * i + t] / s4[t];
             }
-            amax = 0.0f;
+            bamax = 0.0f;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(xh[t]));
-            amax = fmaxf(amax, __shfl_xor(amax, 16));
-            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            for (int t = 0; t < 16; ++t) bamax = fmaxf(bamax, fabsf(xh[t]));
+            bamax = fmaxf(bamax, __shfl_xor(bamax, 16));
+            amax = fmaxf(bamax, __shfl_xor(bamax, 32));
         }
         const float scale = amax / 7.0f;
         // code = RNE(fp32(x_hat / scale)), the quotient again via fp64
         const double rscale = scale != 0.0f ? 1.0 / (double)scale : 0.0;
-        if constexpr (!kFp6) {
+        if constexpr (kFmt == kMx) {
+            // MXFP4: the lane's 16 channels lie in block 2g + quad / 2; its
+            // codes are x_hat / 2^e (exact, a power of two: 2^-e is a normal
+            // fp32 for every clamped e) in E2M1, 8 bytes at byte 8 (quad % 2)
+            // of the row's 16-byte half h = quad / 2 of the group
+            const int e = mx_exponent(bamax);
+            const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
+            uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+            for (int t = 0; t < 16; ++t) packed[t >> 3] |= e2m1_code(xh[t] * inv) << (4 * (t & 7));
+            if (row_ok) {
+                const int b0 = m & ~127;
+                const int nb = min(128, M - b0);
+                uint8_t *dst = qx + (size_t)b0 * (K / 2) + (size_t)g * nb * 32 + (size_t)(quad >> 1) * nb * 16 +
+                               (size_t)(m - b0) * 16 + 8 * (quad & 1);
+                *reinterpret_cast<u32x2 *>(dst) = u32x2{packed[0], packed[1]};
+                if ((quad & 1) == 0)
+                    static_cast<uint8_t *>(sx_out)[(size_t)(2 * g + (quad >> 1)) * sx_ld + m] = (uint8_t)(e + 127);
+            }
+        } else if constexpr (kFmt == kInt4) {
             // INT4 container: two's-complement nibbles, low nibble = even k
             uint32_t packed[2] = {0u, 0u};
             if (scale != 0.0f) {
@@ -188,7 +234,8 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
                 *d2 = w[2];
             }
         }
-        if (row_ok && quad == 0) sx[(size_t)g * M + m] = scale;
+        if constexpr (kFmt != kMx)
+            if (row_ok && quad == 0) static_cast<float *>(sx_out)[(size_t)g * M + m] = scale;
 
         // low-rank down-projection on raw X (1/s folded into L1s)
 #pragma unroll
@@ -267,29 +314,44 @@ __global__ __launch_bounds__(256) void channel_absmax_kernel(const uint16_t *__r
 }  // namespace
 
 template <int RT>
-static void launch_act_rt(dim3 grid, hipStream_t stream, bool fp6, const uint16_t *X, const float *smooth,
-                          const uint16_t *l1t, int M, int K, int rank, uint8_t *qx, float *sx, uint16_t *T) {
-    if (fp6)
-        hipLaunchKernelGGL((quantize_act_kernel<true, RT>), grid, dim3(kActWaves * 64), 0, stream, X, smooth,
-                           l1t, M, K, rank, qx, sx, T);
+static void launch_act_rt(dim3 grid, hipStream_t stream, int fmt, const uint16_t *X, const float *smooth,
+                          const uint16_t *l1t, int M, int K, int rank, uint8_t *qx, void *sx, int sx_ld,
+                          uint16_t *T) {
+    if (fmt == kFp6)
+        hipLaunchKernelGGL((quantize_act_kernel<kFp6, RT>), grid, dim3(kActWaves * 64), 0, stream, X, smooth,
+                           l1t, M, K, rank, qx, sx, sx_ld, T);
+    else if (fmt == kMx)
+        hipLaunchKernelGGL((quantize_act_kernel<kMx, RT>), grid, dim3(kActWaves * 64), 0, stream, X, smooth,
+                           l1t, M, K, rank, qx, sx, sx_ld, T);
     else
-        hipLaunchKernelGGL((quantize_act_kernel<false, RT>), grid, dim3(kActWaves * 64), 0, stream, X, smooth,
-                           l1t, M, K, rank, qx, sx, T);
+        hipLaunchKernelGGL((quantize_act_kernel<kInt4, RT>), grid, dim3(kActWaves * 64), 0, stream, X, smooth,
+                           l1t, M, K, rank, qx, sx, sx_ld, T);
+}
+
+static hipError_t launch_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M, int K,
+                             int rank, int fmt, uint8_t *qx, void *sx, int sx_ld, uint16_t *T,
+                             hipStream_t stream) {
+    const dim3 grid((M + kActRows - 1) / kActRows);
+    switch (rank / 16) {  // rank % 16 == 0 and rank <= 64 are checked by the caller
+        case 0: launch_act_rt<0>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T); break;
+        case 1: launch_act_rt<1>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T); break;
+        case 2: launch_act_rt<2>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T); break;
+        case 3: launch_act_rt<3>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T); break;
+        default: launch_act_rt<4>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T); break;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M,
                                int K, int rank, int qfmt, uint8_t *qx, float *sx, uint16_t *T,
                                hipStream_t stream) {
-    const dim3 grid((M + kActRows - 1) / kActRows);
-    const bool fp6 = qfmt == SVDQ_QFMT_FP6;
-    switch (rank / 16) {  // rank % 16 == 0 and rank <= 64 are checked by the caller
-        case 0: launch_act_rt<0>(grid, stream, fp6, X, smooth, l1t, M, K, rank, qx, sx, T); break;
-        case 1: launch_act_rt<1>(grid, stream, fp6, X, smooth, l1t, M, K, rank, qx, sx, T); break;
-        case 2: launch_act_rt<2>(grid, stream, fp6, X, smooth, l1t, M, K, rank, qx, sx, T); break;
-        case 3: launch_act_rt<3>(grid, stream, fp6, X, smooth, l1t, M, K, rank, qx, sx, T); break;
-        default: launch_act_rt<4>(grid, stream, fp6, X, smooth, l1t, M, K, rank, qx, sx, T); break;
-    }
-    return hipGetLastError();
+    return launch_act(X, smooth, l1t, M, K, rank, qfmt == SVDQ_QFMT_FP6 ? kFp6 : kInt4, qx, sx, M, T, stream);
+}
+
+hipError_t launch_mx_quantize_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M,
+                                  int K, int rank, uint8_t *qx, uint8_t *ux, uint16_t *T,
+                                  hipStream_t stream) {
+    return launch_act(X, smooth, l1t, M, K, rank, kMx, qx, ux, (int)mx_scale_ld(M), T, stream);
 }
 
 hipError_t launch_channel_absmax(const uint16_t *X, int M, int K, float *absmax,

@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr int kMaxDevices = 64;
 
 std::mutex g_mutex;
@@ -186,6 +186,25 @@ svdq_status w4a16_prepare_weights(const uint16_t *W, int K, int N, int group, ui
     return svdq::w4a16_prepare_impl(W, K, N, packed);
 }
 
+size_t svdq_mx_scale_ld(int rows) { return rows < 0 ? 0 : svdq::mx_scale_ld(rows); }
+
+svdq_status svdq_mx_prepare_residual(const uint16_t *W, int K, int N, const float *smooth,
+                                     const uint16_t *l1t, const uint16_t *l2t, int rank, uint8_t *qw,
+                                     uint8_t *uw) {
+    if (!W || !smooth || !qw || !uw) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (K <= 0 || N <= 0 || rank < 0) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (K % SVDQ_GROUP || N % 8) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    if (rank > SVDQ_MAX_RANK || rank % 16 || rank > K || rank > N) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    if (rank > 0 && (!l1t || !l2t)) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (!svdq::all_finite_bf16(W, (int64_t)K * N)) return SVDQ_ERR_NUMERICAL;
+    if (rank > 0 && (!svdq::all_finite_bf16(l1t, (int64_t)rank * K) ||
+                     !svdq::all_finite_bf16(l2t, (int64_t)rank * N)))
+        return SVDQ_ERR_NUMERICAL;
+    for (int k = 0; k < K; ++k)
+        if (!std::isfinite(smooth[k]) || !(smooth[k] > 0.0f)) return SVDQ_ERR_NUMERICAL;
+    return svdq::mx_prepare_residual_impl(W, K, N, smooth, l1t, l2t, rank, qw, uw);
+}
+
 // ---------------------------------------------------------------- device ---
 
 svdq_status svdq_channel_absmax(const uint16_t *X, int M, int K, float *absmax, void *stream) {
@@ -294,6 +313,47 @@ svdq_status w4a16_linear(const uint16_t *X, const uint8_t *packed, const uint16_
     if (st != SVDQ_OK) return st;
     if (M == 0) return SVDQ_OK;
     return launched(svdq::launch_w4a16_linear(X, packed, bias, M, N, K, Y, (hipStream_t)stream));
+}
+
+svdq_status svdq_mx_quantize_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M,
+                                 int K, int rank, uint8_t *qx, uint8_t *ux, uint16_t *T, void *stream) {
+    svdq_status st = check_w4a4_shape(M, K, rank, SVDQ_GROUP);
+    if (st != SVDQ_OK) return st;
+    if (!smooth || (M > 0 && (!X || !qx || !ux))) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (rank > 0 && (!l1t || (M > 0 && !T))) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (!aligned16(X) || !aligned16(smooth) || !aligned16(l1t) || !aligned16(qx) || !aligned16(ux) ||
+        !aligned16(T))
+        return SVDQ_ERR_MISALIGNED;
+    if (!fits_buffer(M, K / 2) || !fits_buffer(K / 32, (int64_t)svdq::mx_scale_ld(M)))
+        return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0) return SVDQ_OK;
+    return launched(svdq::launch_mx_quantize_act(X, smooth, rank ? l1t : nullptr, M, K, rank, qx, ux,
+                                                 rank ? T : nullptr, (hipStream_t)stream));
+}
+
+svdq_status svdq_mx_linear(const uint8_t *qx, const uint8_t *ux, const uint16_t *T, const uint8_t *qw,
+                           const uint8_t *uw, const uint16_t *l2t, const uint16_t *bias, int M, int N, int K,
+                           int rank, void *Y, int y_dtype, void *stream) {
+    svdq_status st = check_w4a4_shape(M, K, rank, SVDQ_GROUP);
+    if (st != SVDQ_OK) return st;
+    if (N <= 0) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (N % 8) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    if (y_dtype != SVDQ_BF16 && y_dtype != SVDQ_F32) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (!qw || !uw || (M > 0 && (!qx || !ux || !Y))) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (rank > 0 && (!l2t || (M > 0 && !T))) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (!aligned16(qx) || !aligned16(ux) || !aligned16(T) || !aligned16(qw) || !aligned16(uw) ||
+        !aligned16(l2t) || !aligned16(bias) || !aligned16(Y))
+        return SVDQ_ERR_MISALIGNED;
+    if (!fits_buffer(M, K / 2) || !fits_buffer(N, K / 2) || !fits_buffer(K / 32, (int64_t)svdq::mx_scale_ld(M)) ||
+        !fits_buffer(K / 32, (int64_t)svdq::mx_scale_ld(N)))
+        return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0) return SVDQ_OK;
+    return launched(svdq::launch_mx_linear(qx, ux, rank ? T : nullptr, qw, uw, rank ? l2t : nullptr, bias, M, N,
+                                           K, rank, Y, y_dtype == SVDQ_F32, (hipStream_t)stream));
 }
 
 svdq_status svdq_debug_group_partials(const uint8_t *qx, const uint8_t *qw,

@@ -20,6 +20,10 @@ svdq_status prepare_residual_impl(const uint16_t *W, int K, int N,
                                   const uint16_t *l2t, int rank, uint8_t *qw,
                                   float *sw);
 svdq_status w8a8_prepare_impl(const uint16_t *W, int K, int N, int8_t *qw, float *sw);
+svdq_status mx_prepare_residual_impl(const uint16_t *W, int K, int N, const float *smooth,
+                                     const uint16_t *l1t, const uint16_t *l2t, int rank, uint8_t *qw,
+                                     uint8_t *uw);
+size_t mx_scale_ld(int rows);
 svdq_status w4a16_prepare_impl(const uint16_t *W, int K, int N, uint8_t *packed);
 size_t w4a16_container_bytes(int K, int N);
 svdq_status repack_codes_impl(const uint8_t *q, int rows, int K, int qfmt, uint8_t *out);
@@ -27,7 +31,8 @@ svdq_status truncated_svd(const double *A, int K, int N, int rank, double *U,
                           double *S, double *V);
 bool all_finite_bf16(const uint16_t *p, int64_t n);
 
-// ---- device launchers (act_quant.hip, w4a4_gemm.hip, w4a4_fp6_gemm.hip, w8a8.hip, w4a16.hip) ----
+// ---- device launchers (act_quant.hip, w4a4_gemm.hip, w4a4_fp6_gemm.hip, w8a8.hip, w4a16.hip,
+//      mx_gemm.hip) ----
 // Arguments are validated by the caller; launchers only pick a grid and launch.
 hipError_t launch_channel_absmax(const uint16_t *X, int M, int K, float *absmax,
                                  hipStream_t stream);
@@ -56,6 +61,12 @@ hipError_t launch_w8a8_acc(const int8_t *qx, const int8_t *qw, int M, int N,
                            int K, int32_t *acc, hipStream_t stream);
 size_t w8a8_workspace_size(int M, int K);
 int w4a16_rows_per_block(int M, int K);
+hipError_t launch_mx_quantize_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M,
+                                  int K, int rank, uint8_t *qx, uint8_t *ux, uint16_t *T,
+                                  hipStream_t stream);
+hipError_t launch_mx_linear(const uint8_t *qx, const uint8_t *ux, const uint16_t *T, const uint8_t *qw,
+                            const uint8_t *uw, const uint16_t *l2t, const uint16_t *bias, int M, int N, int K,
+                            int rank, void *Y, bool y_f32, hipStream_t stream);
 hipError_t launch_w4a16_linear(const uint16_t *X, const uint8_t *packed, const uint16_t *bias, int M,
                                int N, int K, uint16_t *Y, hipStream_t stream);
 

@@ -1,0 +1,240 @@
+// The MXFP4 variant of the SVDQuant W4A4 linear: FP4 E2M1 codes with E8M0
+// scales per block of 32 along K (OCP microscaling) on gfx950's scaled MFMA,
+// fused low-rank up-projection and bias.
+//
+// Source: "Hugging Face встроила Nunchaku в Diffusers..." (iitog.ru),
+// "Nunchaku Lite" paragraph (svdq_w4a4 in an INT4 and a 4-bit float variant)
+// and method paragraph (4-bit weights x 4-bit activations with a 16-bit
+// low-rank branch). The 4-bit float format here is MXFP4, gfx950's native
+// one.
+//
+//   acc[n, m] = sum_b 2^(uw[b, n] + ux[b, m]) sum_{k in b} e2m1(qw) e2m1(qx)
+//   y = acc + T L2 + bias  ->  bf16 (nearest even) or fp32
+//
+// One v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in FP4 covers two
+// 32-blocks (a lane's 32 codes are one block, its scale byte that block's
+// E8M0) and accumulates straight into the fp32 tile: the block scales are
+// applied by the matrix core, so unlike the INT4 variant there is no
+// per-group rescale on the vector ALU.
+//
+// Block tile 128 (n) x 128 (m), 4 waves as 2 x 2, wave tile 64 x 64 (2 x 2
+// MFMA tiles of 32 x 32). One LDS stage holds two groups of 64 k: per
+// operand the two groups' [2 halves][rows][16 bytes] tiles exactly as the MX
+// container stores them (rows in blocks of 128, the halves of a group
+// k-block-major, so 16 consecutive rows' 16-byte pieces are contiguous and
+// an MFMA operand read touches every LDS bank once), plus the groups' E8M0
+// bytes. Everything goes straight from global memory to LDS (buffer_load ...
+// lds), 1 KB per operand load and 256 bytes per scale load; stages are double
+// buffered with one barrier per stage. In a block with fewer than 128 rows
+// the copy runs on into the next tile or past the end of the buffer (zeros);
+// those rows feed only outputs that are never stored.
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace svdq {
+
+namespace {
+
+constexpr int MX_BN = 128;
+constexpr int MX_BM = 128;
+constexpr int MX_THREADS = 256;
+constexpr int MX_KG = 2;             // groups of 64 k per LDS stage
+constexpr int MX_TILE = 128 * 32;    // one group of a 128-row block: 4 KB
+constexpr int MX_FP4 = 4;            // MFMA operand format: FP4 E2M1
+
+typedef int32_t mx_i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void mx_lds_void;
+
+struct StageMx {
+    uint8_t a[MX_KG * MX_TILE];   // weights: [group][half][row][16 bytes]
+    uint8_t b[MX_KG * MX_TILE];   // activations
+    uint8_t ua[MX_KG][2][MX_BN];  // E8M0 of the weights: [group][half][row]
+    uint8_t ub[MX_KG][2][MX_BM];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ mx_i32x8 frag4(const uint8_t *p) {
+    const u32x4 x = *reinterpret_cast<const u32x4 *>(p);
+    return mx_i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+}
+
+__global__ __launch_bounds__(MX_THREADS, 2) void mx_linear_kernel(
+    const uint8_t *__restrict__ qx, const uint8_t *__restrict__ ux, const uint16_t *__restrict__ T,
+    const uint8_t *__restrict__ qw, const uint8_t *__restrict__ uw, const uint16_t *__restrict__ l2t,
+    const uint16_t *__restrict__ bias, int M, int N, int K, int ldm, int ldn, int rank,
+    void *__restrict__ Y, bool y_f32, int tiles_n) {
+    __shared__ StageMx stage[2];
+
+    const int tile_n = blockIdx.x % tiles_n;
+    const int tile_m = blockIdx.x / tiles_n;
+    const int n0 = tile_n * MX_BN;
+    const int m0 = tile_m * MX_BM;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave & 1;
+    const int wm = wave >> 1;
+    const int r32 = lane & 31;
+    const int lh = lane >> 5;
+    const int G = K / 64;
+    const int S = (G + MX_KG - 1) / MX_KG;
+    const uint32_t R = (uint32_t)K / 2;
+    const int nbA = min(128, N - n0);  // rows of this block in the weight container
+    const int nbB = min(128, M - m0);
+
+    const __amdgpu_buffer_rsrc_t rw = mx_rsrc(qw, (uint32_t)N * R);
+    const __amdgpu_buffer_rsrc_t rx = mx_rsrc(qx, (uint32_t)M * R);
+    const __amdgpu_buffer_rsrc_t ruw = mx_rsrc(uw, (uint32_t)(K / 32) * (uint32_t)ldn);
+    const __amdgpu_buffer_rsrc_t rux = mx_rsrc(ux, (uint32_t)(K / 32) * (uint32_t)ldm);
+
+    // Per stage the block issues 16 operand loads (per operand and group one
+    // 4 KB tile, four 1 KB loads) and 4 scale loads; wave w takes operand
+    // w / 2 and group w % 2 of the stage for both.
+    const int op_w = wave >> 1, q_w = wave & 1;
+    const uint32_t base_w = (uint32_t)(op_w ? m0 : n0) * R;
+    const uint32_t tstride_w = (uint32_t)(op_w ? nbB : nbA) * 32u;  // bytes per group in the block
+    // scale bytes: lanes 0-31 read half 0 (k-block 2g), lanes 32-63 half 1,
+    // 4 rows per lane; the scale rows are ld bytes apart (ld % 16 == 0)
+    const uint32_t ld_w = (uint32_t)(op_w ? ldm : ldn);
+    const uint32_t soff_w = (uint32_t)lh * ld_w + (uint32_t)(op_w ? m0 : n0) + 4u * (uint32_t)r32;
+
+    auto issue_stage = [&](int s, StageMx &st) {
+        const int g = s * MX_KG + q_w;
+        if (g < G) {
+            const uint32_t t0 = base_w + (uint32_t)g * tstride_w + (uint32_t)lane * 16u;
+            uint8_t *dst = (op_w ? st.b : st.a) + q_w * MX_TILE;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(op_w ? rx : rw, (mx_lds_void *)(dst + i * 1024), 16,
+                                                         t0 + i * 1024, 0, 0, 0);
+            uint8_t *sdst = op_w ? &st.ub[q_w][0][0] : &st.ua[q_w][0][0];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(op_w ? rux : ruw, (mx_lds_void *)sdst, 4,
+                                                     soff_w + (uint32_t)(2 * g) * ld_w, 0, 0, 0);
+        }
+    };
+
+    // this lane's operand byte offsets within a staged group tile: the
+    // container's halves are nb * 16 bytes apart in a block of nb rows
+    int aoff[2], boff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        aoff[i] = lh * nbA * 16 + (wn * 64 + i * 32 + r32) * 16;
+        boff[i] = lh * nbB * 16 + (wm * 64 + i * 32 + r32) * 16;
+    }
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    issue_stage(0, stage[0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int s = 0; s < S; ++s) {
+        const StageMx &cur = stage[s & 1];
+        if (s + 1 < S) issue_stage(s + 1, stage[(s + 1) & 1]);
+        const int ng = min(MX_KG, G - s * MX_KG);
+#pragma unroll
+        for (int q = 0; q < MX_KG; ++q) {
+            if (q >= ng) break;
+            mx_i32x8 a[2], b[2];
+            int sa[2], sb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                a[i] = frag4(cur.a + q * MX_TILE + aoff[i]);
+                b[i] = frag4(cur.b + q * MX_TILE + boff[i]);
+                sa[i] = cur.ua[q][lh][wn * 64 + i * 32 + r32];
+                sb[i] = cur.ub[q][lh][wm * 64 + i * 32 + r32];
+            }
+#pragma unroll
+            for (int in = 0; in < 2; ++in)
+#pragma unroll
+                for (int im = 0; im < 2; ++im)
+                    acc[in][im] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        a[in], b[im], acc[in][im], MX_FP4, MX_FP4, 0, sa[in], 0, sb[im]);
+        }
+        // the next stage's direct-to-LDS loads must have landed before anyone
+        // reads them, and everyone must be done with this stage before it is
+        // refilled
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    // low-rank up-projection T L2 (bf16 MFMA, fp32 accumulation) and bias
+    for (int kk = 0; kk < rank; kk += 16) {
+        bf16x8 la[2], lb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int n = n0 + wn * 64 + i * 32 + r32;
+            const int m = m0 + wm * 64 + i * 32 + r32;
+            u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
+            if (n < N) va = *reinterpret_cast<const u32x4 *>(l2t + (size_t)n * rank + kk + 8 * lh);
+            if (m < M) vb = *reinterpret_cast<const u32x4 *>(T + (size_t)m * rank + kk + 8 * lh);
+            la[i] = __builtin_bit_cast(bf16x8, va);
+            lb[i] = __builtin_bit_cast(bf16x8, vb);
+        }
+#pragma unroll
+        for (int in = 0; in < 2; ++in)
+#pragma unroll
+            for (int im = 0; im < 2; ++im) acc[in][im] = mfma_bf16_32x32x16(la[in], lb[im], acc[in][im]);
+    }
+    // 32x32 output: lane holds column (lane % 32) = token m, rows 8q + 4 lh + t
+    // = output features n
+#pragma unroll
+    for (int in = 0; in < 2; ++in) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int n = n0 + wn * 64 + in * 32 + 8 * qq + 4 * lh;
+            if (n >= N) continue;
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (bias) {
+                const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n);
+                bv[0] = bf16_bits_to_f32(bb[0] & 0xFFFFu);
+                bv[1] = bf16_bits_to_f32(bb[0] >> 16);
+                bv[2] = bf16_bits_to_f32(bb[1] & 0xFFFFu);
+                bv[3] = bf16_bits_to_f32(bb[1] >> 16);
+            }
+#pragma unroll
+            for (int im = 0; im < 2; ++im) {
+                const int m = m0 + wm * 64 + im * 32 + r32;
+                if (m >= M) continue;
+                float v[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * qq + t] + bv[t];
+                if (y_f32) {
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(Y) + (size_t)m * N + n) =
+                        f32x4{v[0], v[1], v[2], v[3]};
+                } else {
+                    const uint32_t lo = bf16x2_bits(v[0], v[1]);
+                    const uint32_t hi = bf16x2_bits(v[2], v[3]);
+                    *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(Y) + (size_t)m * N + n) = u32x2{lo, hi};
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mx_linear(const uint8_t *qx, const uint8_t *ux, const uint16_t *T, const uint8_t *qw,
+                            const uint8_t *uw, const uint16_t *l2t, const uint16_t *bias, int M, int N, int K,
+                            int rank, void *Y, bool y_f32, hipStream_t stream) {
+    const int tiles_n = (N + MX_BN - 1) / MX_BN;
+    const int tiles_m = (M + MX_BM - 1) / MX_BM;
+    hipLaunchKernelGGL(mx_linear_kernel, dim3(tiles_n * tiles_m), dim3(MX_THREADS), 0, stream, qx, ux, T, qw, uw,
+                       l2t, bias, M, N, K, (int)mx_scale_ld(M), (int)mx_scale_ld(N), rank, Y, y_f32, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace svdq

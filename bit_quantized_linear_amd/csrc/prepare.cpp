@@ -296,12 +296,10 @@ static void quantize_group_int4(const float *r, int64_t ld, int n, int8_t *q,
     }
 }
 
-svdq_status prepare_residual_impl(const uint16_t *W, int K, int N,
-                                  const float *smooth, const uint16_t *l1t,
-                                  const uint16_t *l2t, int rank, uint8_t *qw,
-                                  float *sw) {
-    const int G = K / SVDQ_GROUP;
-    // R as fp32 [K x N]
+// R = fp32(s_k (W - L1s L2)) as fp32 [K x N], the product summed over j in
+// ascending order in float64 (each bf16 x bf16 product is exact there).
+static std::vector<float> compute_residual(const uint16_t *W, int K, int N, const float *smooth,
+                                           const uint16_t *l1t, const uint16_t *l2t, int rank) {
     std::vector<float> R((int64_t)K * N);
     std::vector<double> l1((int64_t)K * rank), l2((int64_t)rank * N);
     for (int j = 0; j < rank; ++j)
@@ -311,8 +309,6 @@ svdq_status prepare_residual_impl(const uint16_t *W, int K, int N,
     parallel_for(0, K, [&](int64_t k0, int64_t k1) {
         std::vector<double> d(N);
         for (int64_t k = k0; k < k1; ++k) {
-            // D[k, :] summed over j in ascending order; each bf16 x bf16
-            // product is exact in float64
             std::fill(d.begin(), d.end(), 0.0);
             for (int j = 0; j < rank; ++j) {
                 double a = l1[k * rank + j];
@@ -328,6 +324,15 @@ svdq_status prepare_residual_impl(const uint16_t *W, int K, int N,
             }
         }
     });
+    return R;
+}
+
+svdq_status prepare_residual_impl(const uint16_t *W, int K, int N,
+                                  const float *smooth, const uint16_t *l1t,
+                                  const uint16_t *l2t, int rank, uint8_t *qw,
+                                  float *sw) {
+    const int G = K / SVDQ_GROUP;
+    const std::vector<float> R = compute_residual(W, K, N, smooth, l1t, l2t, rank);
     parallel_for(0, N, [&](int64_t n0, int64_t n1) {
         std::vector<int8_t> codes(K);
         for (int64_t n = n0; n < n1; ++n) {
@@ -386,6 +391,73 @@ svdq_status prepare_weights_impl(const uint16_t *W, int K, int N,
         }
     }
     return prepare_residual_impl(W, K, N, smooth, l1t, l2t, rank, qw, sw);
+}
+
+// ---- MXFP4 (OCP microscaling: FP4 E2M1 elements, E8M0 scale per 32) ----
+
+// E2M1 code of q: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the even
+// mantissa (nearbyint rounds half to even, and in each binade the even
+// multiple of the quantum is the even mantissa), saturating at 6; bit 3 is
+// the sign, and a value that rounds to zero is +0.
+static uint8_t e2m1_code(float q) {
+    const float m = std::fabs(q);
+    float r;
+    if (m < 2.0f)
+        r = std::nearbyint(2.0f * m) * 0.5f;
+    else if (m < 4.0f)
+        r = std::nearbyint(m);
+    else
+        r = std::fmin(6.0f, 2.0f * std::nearbyint(0.5f * m));
+    int c = r < 2.0f ? (int)(2.0f * r) : (r < 4.0f ? (int)r + 2 : (int)(0.5f * r) + 4);
+    if (c != 0 && q < 0.0f) c |= 8;
+    return (uint8_t)c;
+}
+
+// One MX block of 32 values v[i * ld]: e = floor(log2 amax) - 2 clamped to
+// [-127, 127] (-127 for an all-zero block); codes of v / 2^e (a power of
+// two: exact, or an underflow far below E2M1's smallest step).
+static int mx_block(const float *v, int64_t ld, uint8_t *codes) {
+    float amax = 0.0f;
+    for (int i = 0; i < 32; ++i) amax = std::max(amax, std::fabs(v[i * ld]));
+    int e = -127;
+    if (amax > 0.0f) {
+        int x;
+        std::frexp(amax, &x);  // amax = f 2^x, f in [0.5, 1): floor(log2 amax) = x - 1
+        e = std::min(127, std::max(-127, x - 1 - 2));
+    }
+    const float inv = std::ldexp(1.0f, -e);
+    for (int i = 0; i < 32; ++i) codes[i] = e2m1_code(v[i * ld] * inv);
+    return e;
+}
+
+size_t mx_scale_ld(int rows) { return (size_t)((rows + 15) / 16 * 16); }
+
+// Writes row r's codes of k-block kb (32 codes, nibble i at byte i / 2, low
+// nibble for even i) into the MX container of `rows` rows: blocks of 128
+// rows (n_b in the last), group g = kb / 2 of block b0 at b0 K/2 + g n_b 32,
+// half h = kb % 2 at + h n_b 16, row r - b0 at + 16 (r - b0).
+static void mx_put(uint8_t *out, int rows, int K, int r, int kb, const uint8_t *codes) {
+    const int64_t b0 = (int64_t)(r / 128) * 128;
+    const int64_t nb = std::min<int64_t>(128, rows - b0);
+    uint8_t *dst = out + b0 * (K / 2) + (int64_t)(kb / 2) * nb * 32 + (int64_t)(kb % 2) * nb * 16 + (r - b0) * 16;
+    for (int i = 0; i < 16; ++i) dst[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+}
+
+svdq_status mx_prepare_residual_impl(const uint16_t *W, int K, int N, const float *smooth,
+                                     const uint16_t *l1t, const uint16_t *l2t, int rank, uint8_t *qw,
+                                     uint8_t *uw) {
+    const std::vector<float> R = compute_residual(W, K, N, smooth, l1t, l2t, rank);
+    const int64_t ld = (int64_t)mx_scale_ld(N);
+    parallel_for(0, N, [&](int64_t n0, int64_t n1) {
+        uint8_t codes[32];
+        for (int64_t n = n0; n < n1; ++n)
+            for (int kb = 0; kb < K / 32; ++kb) {
+                const int e = mx_block(R.data() + (int64_t)kb * 32 * N + n, N, codes);
+                uw[kb * ld + n] = (uint8_t)(e + 127);
+                mx_put(qw, N, K, (int)n, kb, codes);
+            }
+    });
+    return SVDQ_OK;
 }
 
 svdq_status w8a8_prepare_impl(const uint16_t *W, int K, int N, int8_t *qw, float *sw) {

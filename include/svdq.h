@@ -1,8 +1,8 @@
 /*
  * svdq.h -- C interface of libsvdq.so: the SVDQuant W4A4 linear with its
- * 16-bit low-rank branch, the INT8 tensorwise W8A8 linear and the W4A16
- * linear (4-bit weights, 16-bit activations), for AMD Instinct MI355X
- * (gfx950, CDNA4).
+ * 16-bit low-rank branch (INT4 and MXFP4 variants), the INT8 tensorwise W8A8
+ * linear and the W4A16 linear (4-bit weights, 16-bit activations), for AMD
+ * Instinct MI355X (gfx950, CDNA4).
  *
  * The method (sources, cited by page title and passage):
  *  [HF-SVDQ]   "Hugging Face встроила Nunchaku в Diffusers: диффузия быстрее на
@@ -175,6 +175,44 @@ svdq_status svdq_prepare_residual(const uint16_t *W, int K, int N,
 svdq_status w8a8_prepare_weights(const uint16_t *W, int K, int N,
                                  int8_t *qw, float *sw);
 
+/* ------------------------------------------------ MXFP4 variant (HOST) --- */
+
+/* The 4-bit float variant of the svdq_w4a4 linear [HF-SVDQ "Nunchaku Lite"
+ * paragraph: INT4 and NVFP4 variants; hardware paragraph: the float variant
+ * runs on GPUs with native 4-bit float matrix units]. gfx950's native 4-bit
+ * float format is OCP MXFP4, so the variant is built as MXFP4: FP4 E2M1
+ * codes with one power-of-two E8M0 scale per block of 32 values along K.
+ * Smoothing, the low-rank branch, T and the residual R are those of the INT4
+ * variant (svdq_prepare_weights gives s, l1t, l2t).
+ *   block of 32 (a row of X_hat or a column of R along K): amax = max |v|,
+ *   e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 if amax == 0),
+ *   E8M0 byte e + 127; code = E2M1 of v / 2^e, round to nearest, ties to the
+ *   even mantissa, saturating at 6, a zero result as +0. E2M1: bit 3 sign,
+ *   magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7.
+ * MX code container (qx, qw) of `rows` rows, rows * K/2 bytes: rows in blocks
+ *   of 128 (n_b = min(128, rows - 128b) in block b), block b at byte
+ *   128 b K/2; group g (64 k, two blocks of 32) of the block at + g n_b 32;
+ *   its half h (the 32-block 2g + h) at + h n_b 16; row r of the block at
+ *   + 16 r: 16 bytes, code i of the block in bits [4i, 4i + 4) (byte i / 2,
+ *   low nibble for even i). A buffer is only valid as a whole.
+ * MX scale matrix (ux, uw): E8M0 bytes [K/32][ld], ld = svdq_mx_scale_ld(rows)
+ *   (rows rounded up to a multiple of 16; the padding is never used). */
+
+/* Row stride ld of an MX scale matrix for `rows` rows (0 if rows < 0). */
+size_t svdq_mx_scale_ld(int rows);
+
+/* MXFP4 residual of one weight: R = fp32(s_k (W - L1s L2)) exactly as in
+ * svdq_prepare_residual, each output column's K values quantized in blocks
+ * of 32 as above.
+ * In:  W [K, N] bf16 bits; smooth [K]; l1t [rank, K]; l2t [N, rank] (NULL if
+ *      rank 0). K % 64 == 0, N % 8 == 0, rank % 16 == 0, rank <= 64.
+ * Out: qw: MX code container of N rows (N * K/2 bytes); uw [K/32][ld(N)].
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, NUMERICAL. */
+svdq_status svdq_mx_prepare_residual(const uint16_t *W, int K, int N,
+                                     const float *smooth, const uint16_t *l1t,
+                                     const uint16_t *l2t, int rank,
+                                     uint8_t *qw, uint8_t *uw);
+
 /* Bytes of the W4A16 weight container for a [K, N] weight (0 on a bad
  * argument: K <= 0, N <= 0 or K % 64). */
 size_t w4a16_weight_bytes(int K, int N);
@@ -289,6 +327,40 @@ svdq_status w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
                         const uint16_t *bias, int M, int N, int K,
                         void *workspace, size_t workspace_bytes, uint16_t *Y,
                         void *stream);
+
+/* Fused activation quantization of the MXFP4 variant -- one pass over X:
+ * X_hat = fp32(X / s_k) (IEEE fp32 division, as svdq_quantize_act); per row
+ * and block of 32 along K the E8M0 scale and E2M1 codes above;
+ * T[m, :] = bf16(X[m, :] L1s) as svdq_quantize_act.
+ * In:  X [M, K] bf16; smooth [K]; l1t [rank, K] (NULL if rank 0).
+ * Out: qx: MX code container of M rows; ux [K/32][ld(M)] (16-byte aligned);
+ *      T [M, rank] bf16 (NULL if rank 0). K % 64 == 0, rank % 16 == 0,
+ *      rank <= 64; M == 0 launches nothing.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, MISALIGNED, UNSUPPORTED_DEVICE,
+ *      HIP. */
+svdq_status svdq_mx_quantize_act(const uint16_t *X, const float *smooth,
+                                 const uint16_t *l1t, int M, int K, int rank,
+                                 uint8_t *qx, uint8_t *ux, uint16_t *T,
+                                 void *stream);
+
+/* The MXFP4 linear with fused low-rank up-projection and bias:
+ *   acc[m, n] = sum_b 2^(ex[b, m] + ew[b, n]) sum_{k in b} e2m1(qx) e2m1(qw)
+ *               (the scaled FP4 MFMA: block scales applied by the matrix
+ *               core, fp32 accumulation over the blocks in ascending order)
+ *   y = acc + sum_j T[m, j] L2[j, n] + bias[n]  (bf16 MFMA, fp32)
+ *   Y = y rounded once to bf16 (nearest even) or stored as fp32.
+ * In:  qx, ux (svdq_mx_quantize_act), T [M, rank]; qw, uw
+ *      (svdq_mx_prepare_residual), l2t [N, rank]; bias [N] bf16 or NULL;
+ *      y_dtype SVDQ_BF16 or SVDQ_F32.
+ * Out: Y [M, N]. Shapes: M >= 0, K % 64 == 0, N % 8 == 0, rank % 16 == 0,
+ *      rank <= 64. Deterministic.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, MISALIGNED, UNSUPPORTED_DEVICE,
+ *      HIP. */
+svdq_status svdq_mx_linear(const uint8_t *qx, const uint8_t *ux,
+                           const uint16_t *T, const uint8_t *qw,
+                           const uint8_t *uw, const uint16_t *l2t,
+                           const uint16_t *bias, int M, int N, int K,
+                           int rank, void *Y, int y_dtype, void *stream);
 
 /* The W4A16 linear [HF-SVDQ "Nunchaku Lite" paragraph, awq_w4a16]:
  *   y[m, n] = sum_g sw[g, n] sum_{k in g} X[m, k] q[k, n] + bias[n]

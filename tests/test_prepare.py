@@ -100,3 +100,25 @@ def test_w8a8_prepare_bit_exact():
     qw_l, sw_l = b.w8a8_prepare_weights(W["bits"])
     assert sw_l == float(sw_o)
     assert np.array_equal(qw_l, o8.to_abi(qw_o))
+
+
+@pytest.mark.parametrize("K,N,rank", [(64, 8, 0), (192, 40, 16), (256, 136, 32)])
+def test_mx_residual_matches_the_oracle_bit_exactly(K, N, rank):
+    """svdq_mx_prepare_residual (C++) == oracle/mxfp4.prepare_from_factors on
+    the same smoothing and factors: E2M1 codes and E8M0 exponents, written in
+    the documented container (ragged 128-row blocks for N > 128)."""
+    from oracle import mxfp4 as mx
+    from tests.mx_format import pack_mx_codes, pack_mx_scales, unpack_mx_codes, unpack_mx_scales
+
+    rng = np.random.default_rng(K + N + rank)
+    W = wl.random_bf16(K * 3 + N, (K, N), 0.02)
+    Wv = W["values"].astype(np.float64)
+    s = sq.rn32(rng.uniform(0.5, 2.0, K)).astype(np.float64)
+    L1s = sq.bf16_round(rng.standard_normal((K, rank)) * 0.05)
+    L2 = sq.bf16_round(rng.standard_normal((rank, N)) * 0.05)
+    prep = mx.prepare_from_factors(Wv, s, L1s, L2)
+    out = b.svdq_mx_prepare_residual(W["bits"], s.astype(np.float32), sq.bf16_bits(L1s.T), sq.bf16_bits(L2.T))
+    assert np.array_equal(out["qw"], pack_mx_codes(prep["qw"]))
+    assert np.array_equal(out["uw"], pack_mx_scales(prep["ew"]))
+    assert np.array_equal(unpack_mx_codes(out["qw"], K), prep["qw"])
+    assert np.array_equal(unpack_mx_scales(out["uw"], N), prep["ew"])
