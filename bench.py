@@ -17,7 +17,8 @@ over the whole step (both kernels). The roofline object describes the
 dominant kernel (the GEMM) against the dense peak of the MFMA type it runs on
 (FP6); "pct_int8_roofline" gives the same throughput against the int8 MFMA
 peak. The W8A8 linear on the attention shape is timed the same way and
-reported under "w8a8". The W4A16 linear (the awq_w4a16 layer type) on an
+reported under "w8a8", and the MXFP4 variant of the W4A4 linear on the same
+workload under "mxfp4". The W4A16 linear (the awq_w4a16 layer type) on an
 adaLN-modulation shape is reported under "w4a16" with its own HBM roofline:
 it is a skinny GEMM whose cost is one read of the packed weight. Its rate is
 taken the way a model runs such layers, one per block with distinct weights:
@@ -77,6 +78,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-w8a8", action="store_true")
     p.add_argument("--no-w4a16", action="store_true")
+    p.add_argument("--no-mx", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=4608,
                    help="token rows of the workload the CPU oracle is timed on")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -469,6 +471,41 @@ def main():
         "cold_step_ms_min": round(float(np.min(cold)), 5),
         "outputs_finite": y_finite,
     }
+
+    if not args.no_mx:
+        # the MXFP4 variant on the same workload and the same smoothing and
+        # low-rank factors: E2M1 codes with E8M0 block-32 scales
+        t1 = time.perf_counter()
+        mxw = b.svdq_mx_prepare_residual(W["bits"], prep["s"], prep["l1t"], prep["l2t"])
+        mx_prep_s = time.perf_counter() - t1
+        mqw, muw = up(mxw["qw"]), up(mxw["uw"])
+        mqx = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+        mux = torch.empty((K // 32, b.svdq_mx_scale_ld(M)), dtype=torch.uint8, device="cuda")
+
+        def actmx():
+            b.svdq_mx_quantize_act(Xd, s_d, l1_d, mqx, mux, T, r)
+
+        def gemmmx():
+            b.svdq_mx_linear(mqx, mux, T, mqw, muw, l2_d, b_d, Y, M, N, K, r)
+
+        msmx, permx, _, eachmx = time_steps([actmx, gemmmx], args.steps, args.warmup)
+        mx_tops = ops / (msmx * 1e-3) / 1e12
+        mx_gemm_tops = ops / (permx[1] * 1e-3) / 1e12
+        out["mxfp4"] = {
+            "workload": f"{case.name}: SVDQuant W4A4 linear, MXFP4 variant (E2M1, E8M0 per 32 along K), "
+                        f"M={M} K={K} N={N} rank={r}",
+            "ms_per_step": round(msmx, 5), "TOPS": round(mx_tops, 2),
+            "pct_int8_roofline": round(100.0 * mx_tops / INT8_PEAK_TOPS, 2),
+            "step_ms_median": round(float(np.median(eachmx)), 5),
+            "act_ms": round(permx[0], 5), "gemm_ms": round(permx[1], 5),
+            "roofline": {"bound": "mfma", "kernel": "svdq_mx_linear", "mfma_dtype": "fp4",
+                         "achieved": round(mx_gemm_tops, 2), "peak": FP6_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(mx_gemm_tops / FP6_PEAK_TFLOPS, 4), "traffic": None,
+                         "algorithmic_ops": ops},
+            "prepare_residual_library_s": round(mx_prep_s, 3),
+        }
+        log(f"[bench] mxfp4: step {msmx:.4f} ms (act {permx[0]:.4f} ms, gemm {permx[1]:.4f} ms) "
+            f"-> {mx_tops:.1f} TOPS")
 
     if not args.no_w8a8:
         c8 = wl.CASES["w8a8_attn"]
