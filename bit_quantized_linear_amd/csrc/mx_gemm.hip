@@ -24,8 +24,10 @@
 // k-block-major, so 16 consecutive rows' 16-byte pieces are contiguous and
 // an MFMA operand read touches every LDS bank once), plus the groups' E8M0
 // bytes. Everything goes straight from global memory to LDS (buffer_load ...
-// lds), 1 KB per operand load and 256 bytes per scale load; stages are double
-// buffered with one barrier per stage. In a block with fewer than 128 rows
+// lds), 1 KB per operand load and 256 bytes per scale load. Three stages
+// rotate: while one is read, the next two are in flight (a stage holds only
+// eight MFMAs per wave, far less than a load's latency), with one barrier
+// per stage. In a block with fewer than 128 rows
 // the copy runs on into the next tile or past the end of the buffer (zeros);
 // those rows feed only outputs that are never stored.
 
@@ -42,6 +44,7 @@ constexpr int MX_BN = 128;
 constexpr int MX_BM = 128;
 constexpr int MX_THREADS = 256;
 constexpr int MX_KG = 2;             // groups of 64 k per LDS stage
+constexpr int MX_NS = 3;             // LDS stages: two in flight while one is read
 constexpr int MX_TILE = 128 * 32;    // one group of a 128-row block: 4 KB
 constexpr int MX_FP4 = 4;            // MFMA operand format: FP4 E2M1
 
@@ -64,12 +67,12 @@ __device__ __forceinline__ mx_i32x8 frag4(const uint8_t *p) {
     return mx_i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
 }
 
-__global__ __launch_bounds__(MX_THREADS, 2) void mx_linear_kernel(
+__global__ __launch_bounds__(MX_THREADS, 3) void mx_linear_kernel(
     const uint8_t *__restrict__ qx, const uint8_t *__restrict__ ux, const uint16_t *__restrict__ T,
     const uint8_t *__restrict__ qw, const uint8_t *__restrict__ uw, const uint16_t *__restrict__ l2t,
     const uint16_t *__restrict__ bias, int M, int N, int K, int ldm, int ldn, int rank,
     void *__restrict__ Y, bool y_f32, int tiles_n) {
-    __shared__ StageMx stage[2];
+    __shared__ StageMx stage[MX_NS];
 
     const int tile_n = blockIdx.x % tiles_n;
     const int tile_m = blockIdx.x / tiles_n;
@@ -136,38 +139,55 @@ __global__ __launch_bounds__(MX_THREADS, 2) void mx_linear_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+    // loads this wave issues for stage t (operand tile + scales, or none
+    // past K): the explicit waits below count them
+    auto loads_of = [&](int t) { return (t < S && t * MX_KG + q_w < G) ? 5 : 0; };
+    // wait until at most `pending` of this wave's loads are outstanding
+    // (0 or 5: vmcnt is an immediate)
+    auto wait_loads = [&](int pending) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (pending)
+            __builtin_amdgcn_s_waitcnt(5 | (7 << 4) | (0 << 8));  // vmcnt(5) lgkmcnt(0)
+        else
+            __builtin_amdgcn_s_waitcnt(0);
+    };
+
     issue_stage(0, stage[0]);
-    __builtin_amdgcn_s_waitcnt(0);
+    if (S > 1) issue_stage(1, stage[1]);
+    wait_loads(loads_of(1));
     __syncthreads();
 
     for (int s = 0; s < S; ++s) {
-        const StageMx &cur = stage[s & 1];
-        if (s + 1 < S) issue_stage(s + 1, stage[(s + 1) & 1]);
+        const StageMx &cur = stage[s % MX_NS];
+        if (s + 2 < S) issue_stage(s + 2, stage[(s + 2) % MX_NS]);
         const int ng = min(MX_KG, G - s * MX_KG);
+        mx_i32x8 a[MX_KG][2], b[MX_KG][2];
+        int sa[MX_KG][2], sb[MX_KG][2];
 #pragma unroll
         for (int q = 0; q < MX_KG; ++q) {
             if (q >= ng) break;
-            mx_i32x8 a[2], b[2];
-            int sa[2], sb[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                a[i] = frag4(cur.a + q * MX_TILE + aoff[i]);
-                b[i] = frag4(cur.b + q * MX_TILE + boff[i]);
-                sa[i] = cur.ua[q][lh][wn * 64 + i * 32 + r32];
-                sb[i] = cur.ub[q][lh][wm * 64 + i * 32 + r32];
+                a[q][i] = frag4(cur.a + q * MX_TILE + aoff[i]);
+                b[q][i] = frag4(cur.b + q * MX_TILE + boff[i]);
+                sa[q][i] = cur.ua[q][lh][wn * 64 + i * 32 + r32];
+                sb[q][i] = cur.ub[q][lh][wm * 64 + i * 32 + r32];
             }
+        }
+#pragma unroll
+        for (int q = 0; q < MX_KG; ++q) {
+            if (q >= ng) break;
 #pragma unroll
             for (int in = 0; in < 2; ++in)
 #pragma unroll
                 for (int im = 0; im < 2; ++im)
                     acc[in][im] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        a[in], b[im], acc[in][im], MX_FP4, MX_FP4, 0, sa[in], 0, sb[im]);
+                        a[q][in], b[q][im], acc[in][im], MX_FP4, MX_FP4, 0, sa[q][in], 0, sb[q][im]);
         }
-        // the next stage's direct-to-LDS loads must have landed before anyone
-        // reads them, and everyone must be done with this stage before it is
-        // refilled
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0);
+        // stage s + 1 must have landed before anyone reads it (stage s + 2
+        // may stay in flight), and everyone must be done with stage s before
+        // it is refilled (with stage s + 3, issued after the barrier)
+        wait_loads(loads_of(s + 2));
         __syncthreads();
     }
 
@@ -189,40 +209,10 @@ __global__ __launch_bounds__(MX_THREADS, 2) void mx_linear_kernel(
 #pragma unroll
             for (int im = 0; im < 2; ++im) acc[in][im] = mfma_bf16_32x32x16(la[in], lb[im], acc[in][im]);
     }
-    // 32x32 output: lane holds column (lane % 32) = token m, rows 8q + 4 lh + t
-    // = output features n
-#pragma unroll
-    for (int in = 0; in < 2; ++in) {
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-            const int n = n0 + wn * 64 + in * 32 + 8 * qq + 4 * lh;
-            if (n >= N) continue;
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (bias) {
-                const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n);
-                bv[0] = bf16_bits_to_f32(bb[0] & 0xFFFFu);
-                bv[1] = bf16_bits_to_f32(bb[0] >> 16);
-                bv[2] = bf16_bits_to_f32(bb[1] & 0xFFFFu);
-                bv[3] = bf16_bits_to_f32(bb[1] >> 16);
-            }
-#pragma unroll
-            for (int im = 0; im < 2; ++im) {
-                const int m = m0 + wm * 64 + im * 32 + r32;
-                if (m >= M) continue;
-                float v[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * qq + t] + bv[t];
-                if (y_f32) {
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(Y) + (size_t)m * N + n) =
-                        f32x4{v[0], v[1], v[2], v[3]};
-                } else {
-                    const uint32_t lo = bf16x2_bits(v[0], v[1]);
-                    const uint32_t hi = bf16x2_bits(v[2], v[3]);
-                    *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(Y) + (size_t)m * N + n) = u32x2{lo, hi};
-                }
-            }
-        }
-    }
+    // every load has landed and been read: the stage buffers hold the
+    // output tile on its way out
+    static_assert(sizeof(StageMx) * MX_NS >= kTileStoreLdsBytes, "LDS too small for the output tile");
+    store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias, Y, y_f32, M, N, m0, n0, wn, wm, tid);
 }
 
 }  // namespace

@@ -137,39 +137,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void w4a4_gemm_kernel(
 #pragma unroll
                 for (int im = 0; im < 2; ++im) acc[in][im] = mfma_bf16_32x32x16(a[in], b[im], acc[in][im]);
         }
-        // bias and store: each lane writes 4 consecutive n of one token row
-#pragma unroll
-        for (int in = 0; in < 2; ++in) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * 64 + in * 32 + 8 * q + 4 * lh;
-                if (n >= N) continue;
-                float bv[4] = {0.f, 0.f, 0.f, 0.f};
-                if (bias) {
-                    const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n);
-                    bv[0] = bf16_bits_to_f32(bb[0] & 0xFFFFu);
-                    bv[1] = bf16_bits_to_f32(bb[0] >> 16);
-                    bv[2] = bf16_bits_to_f32(bb[1] & 0xFFFFu);
-                    bv[3] = bf16_bits_to_f32(bb[1] >> 16);
-                }
-#pragma unroll
-                for (int im = 0; im < 2; ++im) {
-                    const int m = m0 + wm * 64 + im * 32 + r32;
-                    if (m >= M) continue;
-                    float v[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * q + t] + bv[t];
-                    if (y_f32) {
-                        *reinterpret_cast<f32x4 *>(static_cast<float *>(Y) + (size_t)m * N + n) =
-                            f32x4{v[0], v[1], v[2], v[3]};
-                    } else {
-                        const uint32_t lo = bf16x2_bits(v[0], v[1]);
-                        const uint32_t hi = bf16x2_bits(v[2], v[3]);
-                        *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(Y) + (size_t)m * N + n) = u32x2{lo, hi};
-                    }
-                }
-            }
-        }
+        // every stage has been read: the stage buffers hold the output tile on
+        // its way out
+        static_assert(sizeof(GemmStage) * 2 >= kTileStoreLdsBytes, "LDS too small for the output tile");
+        store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias, Y, y_f32, M, N, m0, n0, wn, wm,
+                           threadIdx.x);
     }
 }
 

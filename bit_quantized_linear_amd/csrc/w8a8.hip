@@ -217,34 +217,32 @@ __global__ __launch_bounds__(W8_THREADS, 2) void w8a8_gemm_kernel(
         __syncthreads();
     }
 
-    float scale = 0.0f;
-    if constexpr (kEpi == W8Epilogue::kLinear) scale = (*sxp) * sw;
+    if constexpr (kEpi == W8Epilogue::kLinear) {
+        // y = P sx sw + bias, the product rounded to fp32 before the sum
+        const float scale = (*sxp) * sw;
+        f32x16 acc[2][2];
 #pragma unroll
-    for (int in = 0; in < 2; ++in) {
+        for (int in = 0; in < 2; ++in)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int n = n0 + wn * 64 + in * 32 + 8 * q + 4 * lh;
-            if (n >= N) continue;
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (kEpi == W8Epilogue::kLinear && bias) {
-                const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n);
-                bv[0] = bf16_bits_to_f32(bb[0] & 0xFFFFu);
-                bv[1] = bf16_bits_to_f32(bb[0] >> 16);
-                bv[2] = bf16_bits_to_f32(bb[1] & 0xFFFFu);
-                bv[3] = bf16_bits_to_f32(bb[1] >> 16);
-            }
+            for (int im = 0; im < 2; ++im)
 #pragma unroll
-            for (int im = 0; im < 2; ++im) {
-                const int m = m0 + wm * 64 + im * 32 + r32;
-                if (m >= M) continue;
-                if constexpr (kEpi == W8Epilogue::kLinear) {
-                    float v[4];
+                for (int e = 0; e < 16; ++e) acc[in][im][e] = (float)P[in][im][e] * scale;
+        // every stage has been read: the stage buffers hold the output tile
+        // on its way out
+        static_assert(sizeof(W8Stage) * 2 >= kTileStoreLdsBytes, "LDS too small for the output tile");
+        store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias, Y, false, M, N, m0, n0, wn, wm,
+                           threadIdx.x);
+    } else {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = (float)P[in][im][4 * q + t] * scale + bv[t];
-                    const uint32_t lo = bf16x2_bits(v[0], v[1]);
-                    const uint32_t hi = bf16x2_bits(v[2], v[3]);
-                    *reinterpret_cast<u32x2 *>(Y + (size_t)m * N + n) = u32x2{lo, hi};
-                } else {
+        for (int in = 0; in < 2; ++in) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * 64 + in * 32 + 8 * q + 4 * lh;
+                if (n >= N) continue;
+#pragma unroll
+                for (int im = 0; im < 2; ++im) {
+                    const int m = m0 + wm * 64 + im * 32 + r32;
+                    if (m >= M) continue;
                     i32x4 v;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) v[t] = P[in][im][4 * q + t];
