@@ -67,6 +67,9 @@ COPY_KERNEL_KEY = "neg_kernel"
 W16_SOURCES = ("w4a16.hip", "device_common.h")
 W16_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "w4a16_linear_modulation_2x3072x18432_traffic.txt")
 W16_KERNEL_KEY = "w4a16_kernel"
+MX_SOURCES = ("mx_gemm.hip", "device_common.h")
+MX_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "svdq_mx_linear_mlp_up_4608x3072x12288_traffic.txt")
+MX_KERNEL_KEY = "mx_linear_kernel"
 
 
 def parse():
@@ -85,7 +88,7 @@ def parse():
                    help="also run a plain elementwise kernel of known size (for counter runs)")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="print the traffic summary from two rocprofv3 --pmc output folders (no GPU)")
-    p.add_argument("--pmc-kernel", choices=("fp6_gemm", "w4a16"), default="fp6_gemm",
+    p.add_argument("--pmc-kernel", choices=("fp6_gemm", "w4a16", "mx_gemm"), default="fp6_gemm",
                    help="kernel whose traffic --summarize-pmc reports")
     return p.parse_args()
 
@@ -122,6 +125,11 @@ def summarize_pmc(fetch_dir, write_dir, which="fp6_gemm"):
         M, K, N = 2, 3072, 18432
         algo = w4a16_bytes(M, K, N)
         title = f"# HBM traffic of w4a16_linear, modulation M={M} K={K} N={N}"
+    elif which == "mx_gemm":
+        key, sources = MX_KERNEL_KEY, MX_SOURCES
+        M, K, N, r = 4608, 3072, 12288, 32
+        algo = mx_gemm_bytes(M, N, K, r)
+        title = f"# HBM traffic of svdq_mx_linear (MXFP4), mlp_up M={M} K={K} N={N} rank={r}"
     else:
         key, sources = GEMM_KERNEL_KEY, GEMM_SOURCES
         M, K, N, r = 4608, 3072, 12288, 32
@@ -181,6 +189,12 @@ def algorithmic_gemm_bytes(M, N, K, r):
     """Bytes the GEMM must move at least once: both FP6 code matrices (3/4
     byte per code), both scale matrices, T and L2 (bf16), bias, bf16 Y."""
     return (M + N) * (K // 4 * 3) + (K // 64) * (M + N) * 4 + (M + N) * r * 2 + N * 2 + M * N * 2
+
+
+def mx_gemm_bytes(M, N, K, r):
+    """The same for the MXFP4 linear: E2M1 codes (1/2 byte each), E8M0 block
+    scales (one byte per 32 codes), T, L2, bias and bf16 Y."""
+    return (M + N) * (K // 2) + (K // 32) * (M + N) + (M + N) * r * 2 + N * 2 + M * N * 2
 
 
 def log(*a):
@@ -491,6 +505,7 @@ def main():
         msmx, permx, _, eachmx = time_steps([actmx, gemmmx], args.steps, args.warmup)
         mx_tops = ops / (msmx * 1e-3) / 1e12
         mx_gemm_tops = ops / (permx[1] * 1e-3) / 1e12
+        traffic_mx, traffic_mx_detail = read_traffic_summary(MX_TRAFFIC_SUMMARY, MX_SOURCES)
         out["mxfp4"] = {
             "workload": f"{case.name}: SVDQuant W4A4 linear, MXFP4 variant (E2M1, E8M0 per 32 along K), "
                         f"M={M} K={K} N={N} rank={r}",
@@ -500,8 +515,9 @@ def main():
             "act_ms": round(permx[0], 5), "gemm_ms": round(permx[1], 5),
             "roofline": {"bound": "mfma", "kernel": "svdq_mx_linear", "mfma_dtype": "fp4",
                          "achieved": round(mx_gemm_tops, 2), "peak": FP6_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(mx_gemm_tops / FP6_PEAK_TFLOPS, 4), "traffic": None,
-                         "algorithmic_ops": ops},
+                         "frac": round(mx_gemm_tops / FP6_PEAK_TFLOPS, 4), "traffic": traffic_mx,
+                         "traffic_detail": traffic_mx_detail, "algorithmic_ops": ops,
+                         "algorithmic_bytes": mx_gemm_bytes(M, N, K, r)},
             "prepare_residual_library_s": round(mx_prep_s, 3),
         }
         log(f"[bench] mxfp4: step {msmx:.4f} ms (act {permx[0]:.4f} ms, gemm {permx[1]:.4f} ms) "
