@@ -27,11 +27,14 @@ against the pages:
   weights with 16-bit activations for normalization/modulation layers
   (``oracle/w4a16.py``); and the 4-bit float variant of svdq_w4a4, built as
   OCP MXFP4 (``oracle/mxfp4.py``).
+* [HF-SVDQ] the same paragraphs: the MLP pair (up-projection, GELU,
+  down-projection) with the down-projection's activation side produced from
+  the up-projection's output (``oracle/mlp.py``).
 
 Where the pages leave a step open, the reading taken is stated at the
 function that takes it. Parity status of every function is listed in
-``oracle/svdquant.py``, ``oracle/w8a8.py``, ``oracle/w4a16.py`` and
-``oracle/mxfp4.py`` headers.
+``oracle/svdquant.py``, ``oracle/w8a8.py``, ``oracle/w4a16.py``,
+``oracle/mxfp4.py`` and ``oracle/mlp.py`` headers.
 """
 
-from . import mxfp4, svdquant, w4a16, w8a8  # noqa: F401
+from . import mlp, mxfp4, svdquant, w4a16, w8a8  # noqa: F401
