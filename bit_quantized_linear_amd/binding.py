@@ -44,6 +44,10 @@ SIGNATURES = {
     "svdq_channel_absmax": (_i, [_vp, _i, _i, _vp, _vp]),
     "svdq_quantize_act": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "svdq_w4a4_linear": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
+    "svdq_mlp_workspace_bytes": (_sz, [_i, _i, _i]),
+    "svdq_w4a4_linear_gelu_quantize": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _i,
+                                           _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "svdq_debug_gelu_bf16": (_i, [_vp, _vp, _i, _vp]),
     "w8a8_workspace_bytes": (_sz, [_i, _i]),
     "w8a8_linear": (_i, [_vp, _vp, _f, _vp, _i, _i, _i, _vp, _sz, _vp, _vp]),
     "svdq_mx_scale_ld": (_sz, [_i]),
@@ -264,6 +268,27 @@ def svdq_w4a4_linear(qx, sx, T, qw, sw, l2t, bias, Y, M, N, K, rank, group=GROUP
                                 _dev_ptr(sw, 4), _dev_ptr(l2t, 2), _dev_ptr(bias, 2), M, N, K, rank,
                                 group, qfmt, _dev_ptr(Y), y_dtype, _stream(stream))
     _check("svdq_w4a4_linear", st)
+
+
+def svdq_mlp_workspace_bytes(M, N, rank_down) -> int:
+    return int(lib().svdq_mlp_workspace_bytes(M, N, rank_down))
+
+
+def svdq_w4a4_linear_gelu_quantize(qx, sx, T, qw, sw, l2t, bias, M, N, K, rank, smooth_down, l1t_down,
+                                   rank_down, qx_down, sx_down, T_down, Y_up=None, workspace=None,
+                                   group=GROUP, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().svdq_w4a4_linear_gelu_quantize(
+        _dev_ptr(qx, 1), _dev_ptr(sx, 4), _dev_ptr(T, 2), _dev_ptr(qw, 1), _dev_ptr(sw, 4), _dev_ptr(l2t, 2),
+        _dev_ptr(bias, 2), M, N, K, rank, group, _dev_ptr(smooth_down, 4), _dev_ptr(l1t_down, 2), rank_down,
+        _dev_ptr(qx_down, 1), _dev_ptr(sx_down, 4), _dev_ptr(T_down, 2), _dev_ptr(Y_up, 2),
+        _dev_ptr(workspace), ws_bytes, _stream(stream))
+    _check("svdq_w4a4_linear_gelu_quantize", st)
+
+
+def svdq_debug_gelu_bf16(y, g, stream=None):
+    st = lib().svdq_debug_gelu_bf16(_dev_ptr(y, 2), _dev_ptr(g, 2), y.numel(), _stream(stream))
+    _check("svdq_debug_gelu_bf16", st)
 
 
 def w8a8_workspace_bytes(M, K) -> int:

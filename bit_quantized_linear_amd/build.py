@@ -4,7 +4,9 @@
 
 HIP sources are compiled by hipcc for gfx950 only; host C++ sources by the
 ROCm clang++. Objects go to ``_build/`` beside this file and the shared
-library to ``libsvdq.so`` in this package directory.
+library to ``libsvdq.so`` in this package directory. The GELU table of the
+fused MLP epilogue is generated first (``gelu_table.py`` ->
+``_build/gelu_table.h``).
 """
 
 from __future__ import annotations
@@ -15,6 +17,12 @@ import os
 import shutil
 import subprocess
 import sys
+
+if __package__:
+    from . import gelu_table
+else:  # run as a script
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from bit_quantized_linear_amd import gelu_table
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -47,10 +55,12 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    gelu_table.write(os.path.join(BUILD, "gelu_table.h"))
     jobs = []
     for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        jobs.append([HIPCC] + HIP_FLAGS + HIP_EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj])
+        jobs.append([HIPCC] + HIP_FLAGS + ["-I", BUILD] + HIP_EXTRA.get(os.path.basename(src), []) +
+                    ["-c", src, "-o", obj])
     for src in sorted(glob.glob(os.path.join(CSRC, "*.cpp"))):
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
         jobs.append([CLANGXX] + CXX_FLAGS + ["-c", src, "-o", obj])

@@ -11,6 +11,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "quant_common.h"
 
 namespace svdq {
 
@@ -27,23 +28,6 @@ constexpr int kActRows = 16;   // token rows per block (one 16x16 MFMA row tile)
 // rank tile (8 channels each); B comes from l1t with the same channel
 // mapping. The 8 waves' fp32 partial T tiles are summed in wave order through
 // LDS, so T is deterministic.
-constexpr float kTinyGroup = 0x1p-100f;
-
-// fp32(a / b), correctly rounded, from r = fp64(1 / b) (correctly rounded):
-// d = fp64(a * r) is within 2^-52 (relative) of a / b. A quotient of two
-// fp32 values with 24-bit significands lies either exactly on an fp32 value
-// or at least 2^-49 (relative) away from every fp32 rounding boundary (a
-// midpoint has an odd 25-bit significand; a / b equal to or within 2^-49 of
-// one would need a 49-bit numerator), so d and a / b round to the same fp32
-// value. This holds while the result is a normal fp32 number or overflows;
-// results below 2^-126 can fall on a subnormal midpoint, which the caller
-// excludes (groups whose largest |x / s| is below 2^-100 use IEEE division,
-// and in any other group a subnormal x / s becomes code 0 whatever its
-// exact value, as it is below 7 * 2^-26 of the scale).
-__device__ __forceinline__ float quotient_fp32(float a, double r) {
-    return (float)((double)a * r);
-}
-
 // E2M1 code of q (|q| < 8): nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to
 // the even mantissa (rintf rounds half to even, and in each binade the even
 // multiple of the quantum is the even mantissa), saturating at 6; bit 3 is
@@ -184,9 +168,7 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
             if (scale != 0.0f) {
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
-                    float q = rintf(quotient_fp32(xh[t], rscale));  // round half to even
-                    q = fminf(7.0f, fmaxf(-7.0f, q));
-                    const uint32_t nib = (uint32_t)((int)q) & 0xFu;
+                    const uint32_t nib = (uint32_t)int4_code(xh[t], rscale) & 0xFu;
                     packed[t >> 3] |= nib << (4 * (t & 7));
                 }
             }
@@ -203,10 +185,7 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
             if (scale != 0.0f) {
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
-                    float q = rintf(quotient_fp32(xh[t], rscale));  // round half to even
-                    q = fminf(7.0f, fmaxf(-7.0f, q));
-                    const int qi = (int)q;
-                    const uint32_t v = (qi < 0 ? 0x20u : 0u) | (uint32_t)(qi < 0 ? -qi : qi);
+                    const uint32_t v = fp6_field(int4_code(xh[t], rscale));
                     const int bit = 6 * t;
                     w[bit >> 5] |= v << (bit & 31);
                     if ((bit & 31) > 26) w[(bit >> 5) + 1] |= v >> (32 - (bit & 31));

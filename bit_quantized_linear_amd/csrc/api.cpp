@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 constexpr int kMaxDevices = 64;
 
 std::mutex g_mutex;
@@ -235,6 +235,58 @@ svdq_status svdq_quantize_act(const uint16_t *X, const float *smooth,
     if (M == 0) return SVDQ_OK;
     return launched(svdq::launch_quantize_act(X, smooth, rank ? l1t : nullptr, M, K, rank, qfmt, qx, sx,
                                               rank ? T : nullptr, (hipStream_t)stream));
+}
+
+size_t svdq_mlp_workspace_bytes(int M, int N, int rank_down) {
+    if (M < 0 || N <= 0 || rank_down < 0) return 0;
+    return (size_t)svdq::mlp_tiles_n(N) * (size_t)M * (size_t)rank_down * sizeof(float);
+}
+
+svdq_status svdq_w4a4_linear_gelu_quantize(const uint8_t *qx, const float *sx, const uint16_t *T,
+                                           const uint8_t *qw, const float *sw, const uint16_t *l2t,
+                                           const uint16_t *bias, int M, int N, int K, int rank, int group,
+                                           const float *smooth_down, const uint16_t *l1t_down, int rank_down,
+                                           uint8_t *qx_down, float *sx_down, uint16_t *T_down, uint16_t *Y_up,
+                                           void *workspace, size_t workspace_bytes, void *stream) {
+    svdq_status st = check_w4a4_shape(M, K, rank, group);
+    if (st != SVDQ_OK) return st;
+    if (N <= 0) return SVDQ_ERR_INVALID_ARGUMENT;
+    st = check_w4a4_shape(M, N, rank_down, group);  // the down-projection's K is N
+    if (st != SVDQ_OK) return st;
+    if (!qw || !sw || !smooth_down || (M > 0 && (!qx || !sx || !qx_down || !sx_down)))
+        return SVDQ_ERR_INVALID_ARGUMENT;
+    if (rank > 0 && (!l2t || (M > 0 && !T))) return SVDQ_ERR_INVALID_ARGUMENT;
+    const size_t ws = svdq_mlp_workspace_bytes(M, N, rank_down);
+    if (rank_down > 0 && (!l1t_down || (M > 0 && (!T_down || !workspace || workspace_bytes < ws))))
+        return SVDQ_ERR_INVALID_ARGUMENT;
+    if (!aligned16(qx) || !aligned16(sx) || !aligned16(T) || !aligned16(qw) || !aligned16(sw) ||
+        !aligned16(l2t) || !aligned16(bias) || !aligned16(smooth_down) || !aligned16(l1t_down) ||
+        !aligned16(qx_down) || !aligned16(sx_down) || !aligned16(T_down) || !aligned16(Y_up) ||
+        !aligned16(workspace))
+        return SVDQ_ERR_MISALIGNED;
+    {
+        const int64_t rb = (int64_t)svdq_qrow_bytes(K, SVDQ_QFMT_FP6);
+        if (!fits_buffer(M, rb) || !fits_buffer(N, rb) || !fits_buffer(K / SVDQ_GROUP, 4LL * M) ||
+            !fits_buffer(K / SVDQ_GROUP, 4LL * N) || !fits_buffer(M, (int64_t)svdq_qrow_bytes(N, SVDQ_QFMT_FP6)))
+            return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    }
+    st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0) return SVDQ_OK;
+    svdq::MlpOut out{smooth_down, rank_down ? l1t_down : nullptr, rank_down, qx_down, sx_down,
+                     rank_down ? static_cast<float *>(workspace) : nullptr, Y_up};
+    st = launched(svdq::launch_w4a4_fp6_mlp(qx, sx, rank ? T : nullptr, qw, sw, rank ? l2t : nullptr, bias, M, N,
+                                            K, rank, out, (hipStream_t)stream));
+    if (st != SVDQ_OK || rank_down == 0) return st;
+    return launched(svdq::launch_tpart_reduce(static_cast<const float *>(workspace), svdq::mlp_tiles_n(N), M,
+                                              rank_down, T_down, (hipStream_t)stream));
+}
+
+svdq_status svdq_debug_gelu_bf16(const uint16_t *y, uint16_t *g, int n, void *stream) {
+    if (n < 0 || (n > 0 && (!y || !g))) return SVDQ_ERR_INVALID_ARGUMENT;
+    svdq_status st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    return launched(svdq::launch_gelu_bf16(y, g, n, (hipStream_t)stream));
 }
 
 svdq_status svdq_w4a4_linear(const uint8_t *qx, const float *sx,

@@ -54,6 +54,25 @@ hipError_t launch_w4a4_fp6_linear(const uint8_t *qx, const float *sx,
                                   int rank, void *Y, bool y_f32, hipStream_t stream);
 hipError_t launch_w4a4_fp6_partials(const uint8_t *qx, const uint8_t *qw, int M,
                                     int N, int K, int32_t *P, hipStream_t stream);
+// What the fused MLP epilogue emits for the down-projection (K_down = N of
+// the up-projection): FP6 codes qx [M rows, N], group scales sx [N / 64, M],
+// fp32 partial sums tpart [tiles_n][M][rank] of g L1s over each 128-column
+// tile, and optionally the bf16 up-projection output y_up [M, N].
+struct MlpOut {
+    const float *smooth;  // [N] smoothing factors of the down-projection
+    const uint16_t *l1t;  // [rank, N] its low-rank down factor, transposed
+    int rank;
+    uint8_t *qx;
+    float *sx;
+    float *tpart;
+    uint16_t *y_up;       // may be null
+};
+int mlp_tiles_n(int N);
+hipError_t launch_w4a4_fp6_mlp(const uint8_t *qx, const float *sx, const uint16_t *T, const uint8_t *qw,
+                               const float *sw, const uint16_t *l2t, const uint16_t *bias, int M, int N, int K,
+                               int rank, const MlpOut &out, hipStream_t stream);
+hipError_t launch_tpart_reduce(const float *tpart, int parts, int M, int rank, uint16_t *T, hipStream_t stream);
+hipError_t launch_gelu_bf16(const uint16_t *y, uint16_t *g, int n, hipStream_t stream);
 hipError_t launch_w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
                               const uint16_t *bias, int M, int N, int K,
                               void *workspace, uint16_t *Y, hipStream_t stream);

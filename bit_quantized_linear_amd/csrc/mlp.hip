@@ -1,0 +1,58 @@
+// The MLP pair on the device, second half: the down-projection's low-rank T
+// from the per-column-tile partial sums the up-projection's MLP epilogue
+// wrote, and the GELU rule applied elementwise (a debug entry point that lets
+// the device's GELU be checked on every bf16 input).
+//
+// Source: "Hugging Face встроила Nunchaku в Diffusers..." (iitog.ru), method
+// paragraph (the 16-bit low-rank branch: T = X L1s rounded once to bf16) and
+// "Nunchaku Lite" paragraph (svdq_w4a4 on the MLP projections, fused kernels).
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "gelu.h"
+#include "internal.h"
+
+namespace svdq {
+
+namespace {
+
+// T[m, j] = bf16(sum over column tiles c, in ascending order, of
+// tpart[c, m, j]): one thread per element, deterministic.
+__global__ __launch_bounds__(256) void tpart_reduce_kernel(const float *__restrict__ tpart, int parts, int M,
+                                                           int rank, uint16_t *__restrict__ T) {
+    const size_t n = (size_t)M * rank;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float v = 0.0f;
+    for (int c = 0; c < parts; ++c) v += tpart[(size_t)c * n + i];
+    T[i] = (uint16_t)f32_to_bf16_bits(v);
+}
+
+__global__ __launch_bounds__(256) void gelu_bf16_kernel(const uint16_t *__restrict__ y, uint16_t *__restrict__ g,
+                                                        int n) {
+    __shared__ __attribute__((aligned(16))) uint16_t tab[kGeluTableEntries];
+    for (int i = threadIdx.x; i < kGeluTableEntries / 8; i += 256)
+        reinterpret_cast<u32x4 *>(tab)[i] = reinterpret_cast<const u32x4 *>(kGeluTable)[i];
+    __syncthreads();
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) g[i] = (uint16_t)gelu_bf16_bits(y[i], tab);
+}
+
+}  // namespace
+
+hipError_t launch_tpart_reduce(const float *tpart, int parts, int M, int rank, uint16_t *T, hipStream_t stream) {
+    const size_t n = (size_t)M * rank;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(tpart_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, tpart, parts,
+                       M, rank, T);
+    return hipGetLastError();
+}
+
+hipError_t launch_gelu_bf16(const uint16_t *y, uint16_t *g, int n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(gelu_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, y, g, n);
+    return hipGetLastError();
+}
+
+}  // namespace svdq

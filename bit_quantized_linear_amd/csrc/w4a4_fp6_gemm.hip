@@ -36,11 +36,19 @@
 // 8-byte read of the shared third plane. Stages are double buffered with one
 // barrier per stage; the next stage's loads are in flight during the current
 // stage's MFMAs.
+//
+// The MLP epilogue (an up-projection feeding a down-projection through GELU)
+// does not store y: it rounds y to bf16, applies GELU and quantizes the
+// result for the down-projection in place -- per token row and group of 64
+// output columns the INT4 codes (FP6 container) and the fp32 group scale,
+// and the tile's share of the down-projection's low-rank T.
 
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
+#include "gelu.h"
 #include "internal.h"
+#include "quant_common.h"
 
 namespace svdq {
 
@@ -57,6 +65,11 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int TILE = 128 * GB;  // one group of a 128-row block: 6 KB
+
+// what the kernel does after the main loop
+constexpr int kEpiStore = 0;     // y = acc + T L2 + bias, stored (svdq_w4a4_linear)
+constexpr int kEpiPartials = 1;  // int32 group partials stored per group (debug entry point)
+constexpr int kEpiMlp = 2;       // y -> bf16 -> GELU -> the down-projection's activation side
 
 struct Stage6 {
     uint8_t a[KG * TILE];  // [group][row][48 bytes]
@@ -77,13 +90,225 @@ __device__ __forceinline__ i32x8 frag6(const uint8_t *region, int off16, int off
     return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], 0, 0};
 }
 
-template <bool kLinear>
+// LDS of the MLP epilogue (the stage buffers are free by then): a bf16 tile
+// of 64 rows x 128 columns (rows padded to 264 bytes), 1 / s and s of the
+// tile's 128 channels, and the GELU table.
+constexpr int kMlpPitch = 264;
+constexpr int kMlpRcpOff = 64 * kMlpPitch;
+constexpr int kMlpSOff = kMlpRcpOff + 128 * 8;
+constexpr int kMlpTabOff = kMlpSOff + 128 * 4;
+constexpr int kMlpLdsBytes = kMlpTabOff + kGeluTableEntries * 2;
+
+// The tile's y = acc + bias, in two passes of 64 token rows (the waves of
+// one wm row write their accumulators, rounded to bf16, into the LDS tile).
+// Then thread t takes row t / 4 and the 32 channels 32 (t % 4) of it:
+// (optionally) stores y_up, replaces y by g = GELU(y) in the tile, and
+// quantizes g as the standalone activation pass does: x_hat = fp32(g / s),
+// the group absmax over its 32 channels and the partner thread's (t ^ 1,
+// the other half of the group), scale = absmax / 7, codes by nearest even,
+// written as FP6 fields straight into the down-projection's container (the
+// tile's rows are one 128-row block of it, its 128 columns two groups).
+// Last, wave w multiplies rows 16 w .. 16 w + 15 of the g tile by the
+// tile's 128 rows of L1s (16x16x32 bf16 MFMAs, fp32 accumulation) and
+// stores the fp32 partial of T for this column tile. Columns past N (N is
+// a multiple of 64, so a whole group) give g = 0 and are not written.
+__device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t *lds,
+                                             const uint16_t *__restrict__ bias, const MlpOut &o, int M, int N,
+                                             int m0, int n0, int tile_n, int wn, int wm, int tid) {
+    const int lane = tid & 63, r32 = lane & 31, lh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    double *rcp = reinterpret_cast<double *>(lds + kMlpRcpOff);
+    float *sv = reinterpret_cast<float *>(lds + kMlpSOff);
+    uint16_t *tab = reinterpret_cast<uint16_t *>(lds + kMlpTabOff);
+    if (tid < 128) {
+        const float sg = n0 + tid < N ? o.smooth[n0 + tid] : 1.0f;
+        sv[tid] = sg;
+        rcp[tid] = 1.0 / (double)sg;
+    }
+    for (int i = tid; i < kGeluTableEntries / 8; i += THREADS)
+        reinterpret_cast<u32x4 *>(tab)[i] = reinterpret_cast<const u32x4 *>(kGeluTable)[i];
+
+    const int row = tid >> 2, qd = tid & 3, gl = qd >> 1, half = qd & 1;
+    const bool grp_ok = n0 + 64 * gl < N;
+    const int nb = min(128, M - m0);  // rows of this block of the container
+    const int g_down = 2 * (n0 / 128) + gl;
+    for (int p = 0; p < 2; ++p) {
+        if (wm == p) {
+#pragma unroll
+            for (int in = 0; in < 2; ++in) {
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int nl = wn * 64 + in * 32 + 8 * qq + 4 * lh;
+                    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (bias && n0 + nl < N) {
+                        const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n0 + nl);
+                        bv[0] = bf16_bits_to_f32(bb[0] & 0xFFFFu);
+                        bv[1] = bf16_bits_to_f32(bb[0] >> 16);
+                        bv[2] = bf16_bits_to_f32(bb[1] & 0xFFFFu);
+                        bv[3] = bf16_bits_to_f32(bb[1] >> 16);
+                    }
+#pragma unroll
+                    for (int im = 0; im < 2; ++im) {
+                        const int ml = im * 32 + r32;
+                        float v[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * qq + t] + bv[t];
+                        *reinterpret_cast<u32x2 *>(lds + ml * kMlpPitch + nl * 2) =
+                            u32x2{bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        const int m = m0 + 64 * p + row;
+        uint8_t *rowp = lds + row * kMlpPitch + 64 * qd;
+        uint32_t w[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const u32x2 x = reinterpret_cast<const u32x2 *>(rowp)[i];
+            w[2 * i] = x[0];
+            w[2 * i + 1] = x[1];
+        }
+        if (o.y_up && grp_ok && m < M) {
+            uint16_t *dst = o.y_up + (size_t)m * N + n0 + 32 * qd;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                reinterpret_cast<u32x4 *>(dst)[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+        }
+        // g = GELU(y), back into the tile (zero past N)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t lo = gelu_bf16_bits(w[i] & 0xFFFFu, tab);
+            const uint32_t hi = gelu_bf16_bits(w[i] >> 16, tab);
+            w[i] = grp_ok ? (lo | (hi << 16)) : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) reinterpret_cast<u32x2 *>(rowp)[i] = u32x2{w[2 * i], w[2 * i + 1]};
+
+        // x_hat = fp32(g / s): exact through fp64 reciprocals (quotient_fp32).
+        // One sweep for the group absmax, a second one recomputes x_hat for
+        // the codes; both read g and 1 / s back from LDS eight channels at a
+        // time (cheaper in registers than holding 32 quotients)
+        auto chunk = [&](int c, float gv[8]) {
+            // rows are 8-byte aligned (264-byte pitch): two 8-byte reads
+            const u32x2 x0 = reinterpret_cast<const u32x2 *>(rowp)[2 * c];
+            const u32x2 x1 = reinterpret_cast<const u32x2 *>(rowp)[2 * c + 1];
+            const uint32_t x[4] = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                gv[2 * i] = bf16_bits_to_f32(x[i] & 0xFFFFu);
+                gv[2 * i + 1] = bf16_bits_to_f32(x[i] >> 16);
+            }
+        };
+        float amax = 0.0f;
+#pragma unroll 1
+        for (int c = 0; c < 4; ++c) {
+            float gv[8];
+            chunk(c, gv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(quotient_fp32(gv[i], rcp[32 * qd + 8 * c + i])));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        // below the range quotient_fp32 covers: IEEE divisions (both threads
+        // of the group decide alike)
+        const bool tiny = amax < kTinyGroup;
+        if (tiny) {
+            amax = 0.0f;
+#pragma unroll 1
+            for (int c = 0; c < 4; ++c) {
+                float gv[8];
+                chunk(c, gv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(gv[i] / sv[32 * qd + 8 * c + i]));
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 1));
+        }
+        const float scale = amax / 7.0f;
+        const double rscale = scale != 0.0f ? 1.0 / (double)scale : 0.0;
+        // 32 six-bit fields, LSB first: chunk c fills bits [48 c, 48 c + 48)
+        uint32_t fw[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+        if (scale != 0.0f) {
+#pragma unroll 1
+            for (int c = 0; c < 4; ++c) {
+                float gv[8];
+                chunk(c, gv);
+                uint64_t bits48 = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float xh = tiny ? gv[i] / sv[32 * qd + 8 * c + i]
+                                          : quotient_fp32(gv[i], rcp[32 * qd + 8 * c + i]);
+                    bits48 |= (uint64_t)fp6_field(int4_code(xh, rscale)) << (6 * i);
+                }
+                // 48 bits at bit 48 c: chunks 0, 2 start on a word, 1, 3 at bit 16
+                const uint32_t lo = (uint32_t)bits48, hi = (uint32_t)(bits48 >> 32);
+                if (c == 0) { fw[0] = lo; fw[1] = hi; }
+                else if (c == 1) { fw[1] |= lo << 16; fw[2] = (lo >> 16) | (hi << 16); }
+                else if (c == 2) { fw[3] = lo; fw[4] = hi; }
+                else { fw[4] |= lo << 16; fw[5] = (lo >> 16) | (hi << 16); }
+            }
+        }
+        if (grp_ok && m < M) {
+            // the row's 48 bytes of group g_down: this half's 24 bytes H as
+            // H[0:16] at 16 half and H[16:24] at 32 + 8 half
+            uint8_t *rec = o.qx + (size_t)m0 * (size_t)(N / 4 * 3) + ((size_t)g_down * nb + (m - m0)) * GB;
+            *reinterpret_cast<u32x4 *>(rec + 16 * half) = u32x4{fw[0], fw[1], fw[2], fw[3]};
+            *reinterpret_cast<u32x2 *>(rec + 32 + 8 * half) = u32x2{fw[4], fw[5]};
+            if (half == 0) o.sx[(size_t)g_down * M + m] = scale;
+        }
+        __syncthreads();
+
+        // this pass's share of T: rows 16 wave + (lane % 16), channels
+        // 32 step + 8 (lane / 16) + i of the tile
+        if (o.rank > 0) {
+            f32x4 tacc[SVDQ_MAX_RANK / 16];
+#pragma unroll
+            for (int rt = 0; rt < SVDQ_MAX_RANK / 16; ++rt) tacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int ar = 16 * wave + (lane & 15);
+#pragma unroll
+            for (int step = 0; step < 4; ++step) {
+                const int kc = 32 * step + 8 * (lane >> 4);
+                const uint8_t *ap = lds + ar * kMlpPitch + kc * 2;
+                const u32x2 a0 = reinterpret_cast<const u32x2 *>(ap)[0];
+                const u32x2 a1 = reinterpret_cast<const u32x2 *>(ap)[1];
+                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
+                const bool k_ok = n0 + 32 * step < N;
+#pragma unroll
+                for (int rt = 0; rt < SVDQ_MAX_RANK / 16; ++rt) {
+                    if (rt * 16 < o.rank) {
+                        u32x4 bw = {0u, 0u, 0u, 0u};
+                        if (k_ok)
+                            bw = *reinterpret_cast<const u32x4 *>(o.l1t + (size_t)(rt * 16 + (lane & 15)) * N + n0 + kc);
+                        tacc[rt] = mfma_bf16_16x16x32(a, __builtin_bit_cast(bf16x8, bw), tacc[rt]);
+                    }
+                }
+            }
+            // 16x16 output: lane holds column (lane % 16) = rank index within
+            // the tile, rows 4 (lane / 16) + t
+#pragma unroll
+            for (int rt = 0; rt < SVDQ_MAX_RANK / 16; ++rt) {
+                if (rt * 16 < o.rank) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int mt = m0 + 64 * p + 16 * wave + 4 * (lane >> 4) + t;
+                        if (mt < M)
+                            o.tpart[((size_t)tile_n * M + mt) * o.rank + rt * 16 + (lane & 15)] = tacc[rt][t];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int kEpi>
 __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
     const uint8_t *__restrict__ qx, const float *__restrict__ sx, const uint16_t *__restrict__ T,
     const uint8_t *__restrict__ qw, const float *__restrict__ sw, const uint16_t *__restrict__ l2t,
     const uint16_t *__restrict__ bias, int M, int N, int K, int rank, void *__restrict__ Y, bool y_f32,
-    int32_t *__restrict__ Pout, int tiles_n) {
-    __shared__ Stage6 stage[2];
+    int32_t *__restrict__ Pout, int tiles_n, MlpOut mlp) {
+    constexpr bool kLinear = kEpi != kEpiPartials;
+    __shared__ __attribute__((aligned(16))) Stage6 stage[2];
 
     const int tile_n = blockIdx.x % tiles_n;
     const int tile_m = blockIdx.x / tiles_n;
@@ -272,7 +497,12 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
         // every load has landed and been read: the stage buffers hold the
         // output tile on its way out
         static_assert(sizeof(Stage6) * 2 >= kTileStoreLdsBytes, "LDS too small for the output tile");
-        store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias, Y, y_f32, M, N, m0, n0, wn, wm, tid);
+        static_assert(sizeof(Stage6) * 2 >= kMlpLdsBytes, "LDS too small for the MLP epilogue");
+        if constexpr (kEpi == kEpiMlp)
+            mlp_epilogue(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias, mlp, M, N, m0, n0, tile_n, wn, wm, tid);
+        else
+            store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias, Y, y_f32, M, N, m0, n0, wn, wm,
+                               tid);
     }
 }
 
@@ -283,8 +513,20 @@ hipError_t launch_w4a4_fp6_linear(const uint8_t *qx, const float *sx, const uint
                                   int K, int rank, void *Y, bool y_f32, hipStream_t stream) {
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles_m = (M + BM - 1) / BM;
-    hipLaunchKernelGGL(w4a4_fp6_kernel<true>, dim3(tiles_n * tiles_m), dim3(THREADS), 0, stream, qx, sx, T, qw,
-                       sw, l2t, bias, M, N, K, rank, Y, y_f32, nullptr, tiles_n);
+    hipLaunchKernelGGL(w4a4_fp6_kernel<kEpiStore>, dim3(tiles_n * tiles_m), dim3(THREADS), 0, stream, qx, sx, T,
+                       qw, sw, l2t, bias, M, N, K, rank, Y, y_f32, nullptr, tiles_n, MlpOut{});
+    return hipGetLastError();
+}
+
+int mlp_tiles_n(int N) { return (N + BN - 1) / BN; }
+
+hipError_t launch_w4a4_fp6_mlp(const uint8_t *qx, const float *sx, const uint16_t *T, const uint8_t *qw,
+                               const float *sw, const uint16_t *l2t, const uint16_t *bias, int M, int N, int K,
+                               int rank, const MlpOut &out, hipStream_t stream) {
+    const int tiles_n = (N + BN - 1) / BN;
+    const int tiles_m = (M + BM - 1) / BM;
+    hipLaunchKernelGGL(w4a4_fp6_kernel<kEpiMlp>, dim3(tiles_n * tiles_m), dim3(THREADS), 0, stream, qx, sx, T,
+                       qw, sw, l2t, bias, M, N, K, rank, nullptr, false, nullptr, tiles_n, out);
     return hipGetLastError();
 }
 
@@ -292,8 +534,9 @@ hipError_t launch_w4a4_fp6_partials(const uint8_t *qx, const uint8_t *qw, int M,
                                     hipStream_t stream) {
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles_m = (M + BM - 1) / BM;
-    hipLaunchKernelGGL(w4a4_fp6_kernel<false>, dim3(tiles_n * tiles_m), dim3(THREADS), 0, stream, qx, nullptr,
-                       nullptr, qw, nullptr, nullptr, nullptr, M, N, K, 0, nullptr, false, P, tiles_n);
+    hipLaunchKernelGGL(w4a4_fp6_kernel<kEpiPartials>, dim3(tiles_n * tiles_m), dim3(THREADS), 0, stream, qx,
+                       nullptr, nullptr, qw, nullptr, nullptr, nullptr, M, N, K, 0, nullptr, false, P, tiles_n,
+                       MlpOut{});
     return hipGetLastError();
 }
 

@@ -307,6 +307,41 @@ svdq_status svdq_w4a4_linear(const uint8_t *qx, const float *sx,
                              int rank, int group, int qfmt, void *Y,
                              int y_dtype, void *stream);
 
+/* MLP pair on the device [HF-SVDQ method and "Nunchaku Lite" paragraphs:
+ * svdq_w4a4 on the MLP projections, fused kernels]: the up-projection of a
+ * DiT MLP whose output goes through GELU into the down-projection. The
+ * up-projection is svdq_w4a4_linear on the FP6 container; instead of Y it
+ * emits the down-projection's activation side, computed from
+ *   y_up = bf16(acc + T L2 + bias)                 (as svdq_w4a4_linear)
+ *   g    = bf16(GELU(y_up)),  GELU(y) = y Phi(y) = (y / 2) erfc(-y / sqrt 2),
+ *          one correct rounding of the exact value
+ * exactly as svdq_quantize_act would from X = g with K_down = N:
+ *   qx_down [M, svdq_qrow_bytes(N, SVDQ_QFMT_FP6)] (FP6 container),
+ *   sx_down [N/64, M] fp32, T_down [M, rank_down] = bf16(g L1s_down)
+ *   (fp32 partial sums per 128 columns, combined in a fixed order).
+ * In:  the up-projection's operands as svdq_w4a4_linear with qfmt =
+ *      SVDQ_QFMT_FP6 (qx, sx, T, qw, sw, l2t, bias, M, N, K, rank, group);
+ *      smooth_down [N] fp32 and l1t_down [rank_down, N] bf16 (NULL if
+ *      rank_down is 0): the down-projection's smoothing factors and
+ *      transposed low-rank down factor (svdq_prepare_weights of its weight).
+ * Out: qx_down, sx_down, T_down (NULL if rank_down is 0); Y_up [M, N] bf16,
+ *      the up-projection's output, only if not NULL (for checks; the fused
+ *      path does not need it).
+ * Workspace: device memory of svdq_mlp_workspace_bytes(M, N, rank_down)
+ *      bytes (NULL if that is 0), owned by the caller, not read before it is
+ *      written.
+ * Shapes: as svdq_w4a4_linear, plus N % 64 == 0 (the down-projection's K),
+ *      rank_down % 16 == 0, rank_down <= 64. Deterministic.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, MISALIGNED, UNSUPPORTED_DEVICE,
+ *      HIP. */
+size_t svdq_mlp_workspace_bytes(int M, int N, int rank_down);
+svdq_status svdq_w4a4_linear_gelu_quantize(const uint8_t *qx, const float *sx, const uint16_t *T,
+                                           const uint8_t *qw, const float *sw, const uint16_t *l2t,
+                                           const uint16_t *bias, int M, int N, int K, int rank, int group,
+                                           const float *smooth_down, const uint16_t *l1t_down, int rank_down,
+                                           uint8_t *qx_down, float *sx_down, uint16_t *T_down, uint16_t *Y_up,
+                                           void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace w8a8_linear needs for an [M, K] input. */
 size_t w8a8_workspace_bytes(int M, int K);
 
@@ -383,6 +418,12 @@ svdq_status w4a16_linear(const uint16_t *X, const uint8_t *packed,
                          uint16_t *Y, void *stream);
 
 /* ------------------------------------------- TEST-ONLY (same kernels) --- */
+
+/* The device's GELU rule of svdq_w4a4_linear_gelu_quantize applied
+ * elementwise: g[i] = bf16(GELU(y[i])) for n bf16 values (device pointers),
+ * so that it can be checked on every bf16 input. n >= 0.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_DEVICE, HIP. */
+svdq_status svdq_debug_gelu_bf16(const uint16_t *y, uint16_t *g, int n, void *stream);
 
 /* INT4 group partials from the W4A4 GEMM's own main loop (container qfmt):
  *   P[g, m, n] = sum_{k in g} qx[m, k] qw[n, k]  as int32, [K/64, M, N]. */

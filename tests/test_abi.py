@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert b.svdq_version() == 5
+    assert b.svdq_version() == 6
     for s in range(7):
         assert b.status_string(s)
     assert "unknown" in b.status_string(99)
@@ -252,5 +252,39 @@ def test_w4a16_shape_and_argument_checks():
     b.svdq_debug_set_arch_override("gfx942")
     try:
         assert lib.w4a16_linear(FAKE, FAKE, None, 2, 16, 128, 64, FAKE, None) == b.SVDQ_ERR_UNSUPPORTED_DEVICE
+    finally:
+        b.svdq_debug_set_arch_override(None)
+
+
+def _mlp(M=16, N=128, K=128, rank=16, rank_down=16, ws=1 << 20, **kw):
+    a = dict(qx=FAKE, sx=FAKE, T=FAKE, qw=FAKE, sw=FAKE, l2t=FAKE, bias=None, smooth=FAKE, l1t=FAKE, qxd=FAKE,
+             sxd=FAKE, Td=FAKE, yup=None, work=FAKE)
+    a.update(kw)
+    return b.lib().svdq_w4a4_linear_gelu_quantize(
+        a["qx"], a["sx"], a["T"], a["qw"], a["sw"], a["l2t"], a["bias"], M, N, K, rank, 64, a["smooth"], a["l1t"],
+        rank_down, a["qxd"], a["sxd"], a["Td"], a["yup"], a["work"], ws, None)
+
+
+def test_mlp_pair_entry_point_fails_closed():
+    assert b.svdq_mlp_workspace_bytes(4608, 12288, 32) == 96 * 4608 * 32 * 4
+    assert b.svdq_mlp_workspace_bytes(4608, 12288, 0) == 0
+    assert b.svdq_mlp_workspace_bytes(-1, 128, 16) == 0
+    assert _mlp(N=96) == b.SVDQ_ERR_UNSUPPORTED_SHAPE          # the down-projection's K % 64
+    assert _mlp(rank_down=8) == b.SVDQ_ERR_UNSUPPORTED_SHAPE   # rank_down % 16
+    assert _mlp(rank_down=80) == b.SVDQ_ERR_UNSUPPORTED_SHAPE  # rank_down > 64
+    assert _mlp(K=100) == b.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert _mlp(ws=16) == b.SVDQ_ERR_INVALID_ARGUMENT          # workspace too small
+    assert _mlp(work=None) == b.SVDQ_ERR_INVALID_ARGUMENT
+    assert _mlp(smooth=None) == b.SVDQ_ERR_INVALID_ARGUMENT
+    assert _mlp(Td=None) == b.SVDQ_ERR_INVALID_ARGUMENT
+    assert _mlp(qxd=MISALIGNED) == b.SVDQ_ERR_MISALIGNED
+    assert _mlp(yup=MISALIGNED) == b.SVDQ_ERR_MISALIGNED
+    assert _mlp(M=-1) == b.SVDQ_ERR_INVALID_ARGUMENT
+    assert b.lib().svdq_debug_gelu_bf16(None, FAKE, 4, None) == b.SVDQ_ERR_INVALID_ARGUMENT
+    b.svdq_debug_set_arch_override("gfx942")
+    try:
+        assert _mlp() == b.SVDQ_ERR_UNSUPPORTED_DEVICE
+        assert _mlp(rank_down=0, ws=0, work=None, l1t=None, Td=None) == b.SVDQ_ERR_UNSUPPORTED_DEVICE
+        assert b.lib().svdq_debug_gelu_bf16(FAKE, FAKE, 4, None) == b.SVDQ_ERR_UNSUPPORTED_DEVICE
     finally:
         b.svdq_debug_set_arch_override(None)
