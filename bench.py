@@ -80,6 +80,7 @@ def parse():
     p.add_argument("--workload", default="mlp_up")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-w8a8", action="store_true")
+    p.add_argument("--no-mlp", action="store_true")
     p.add_argument("--no-w4a16", action="store_true")
     p.add_argument("--no-mx", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=4608,
@@ -522,6 +523,65 @@ def main():
         }
         log(f"[bench] mxfp4: step {msmx:.4f} ms (act {permx[0]:.4f} ms, gemm {permx[1]:.4f} ms) "
             f"-> {mx_tops:.1f} TOPS")
+
+    if not args.no_mlp:
+        # the whole MLP of the workload: up-projection, GELU, down-projection
+        # (12288 -> 3072), unfused (GELU as its own pass, the down-projection's
+        # activation pass reading GELU(y_up)) and fused (the up-projection's
+        # epilogue emits the down-projection's codes, scales and T)
+        cd = wl.MLP_DOWN
+        Nd, Kd, rd = cd.N, cd.K, cd.rank
+        Wd, bd = wl.mlp_down_weight(), wl.mlp_down_bias()
+        gemm6()
+        G = torch.empty_like(Y)
+        b.svdq_debug_gelu_bf16(Y, G)
+        amax_d = torch.zeros(Kd, dtype=torch.float32, device="cuda")
+        b.svdq_channel_absmax(G, amax_d)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        prep_d = b.svdq_prepare_weights(Wd["bits"], amax_d.cpu().numpy(), rd)
+        mlp_prep_s = time.perf_counter() - t1
+        sd_d, l1d_d, l2d_d, bd_d = up(prep_d["s"]), up(prep_d["l1t"]), up(prep_d["l2t"]), up(bd["bits"])
+        qwd6 = up(b.svdq_repack_codes(prep_d["qw"], Kd, b.QFMT_FP6))
+        swd = up(prep_d["sw"])
+        qxd = torch.empty((M, b.svdq_qrow_bytes(Kd, b.QFMT_FP6)), dtype=torch.uint8, device="cuda")
+        sxd = torch.empty((Kd // 64, M), dtype=torch.float32, device="cuda")
+        Td = torch.empty((M, rd), dtype=torch.int16, device="cuda")
+        Yd = torch.empty((M, Nd), dtype=torch.int16, device="cuda")
+        ws = torch.empty(b.svdq_mlp_workspace_bytes(M, Kd, rd), dtype=torch.uint8, device="cuda")
+
+        def gelu():
+            b.svdq_debug_gelu_bf16(Y, G)
+
+        def act_d():
+            b.svdq_quantize_act(G, sd_d, l1d_d, qxd, sxd, Td, rd, qfmt=b.QFMT_FP6)
+
+        def fused():
+            b.svdq_w4a4_linear_gelu_quantize(qx6, sx, T, qw6_d, sw_d, l2_d, b_d, M, N, K, r, sd_d, l1d_d, rd,
+                                             qxd, sxd, Td, None, ws)
+
+        def gemm_d():
+            b.svdq_w4a4_linear(qxd, sxd, Td, qwd6, swd, l2d_d, bd_d, Yd, M, Nd, Kd, rd, qfmt=b.QFMT_FP6)
+
+        ms_u, per_u, _, _ = time_steps([act6, gemm6, gelu, act_d, gemm_d], args.steps, args.warmup)
+        ms_f, per_f, _, each_f = time_steps([act6, fused, gemm_d], args.steps, args.warmup)
+        ops2 = 2.0 * ops
+        out["mlp_pair"] = {
+            "workload": f"MLP of the {case.name} workload: up M={M} K={K} N={N}, GELU, down K={Kd} N={Nd}, "
+                        f"ranks {r}/{rd}, FP6 container",
+            "fused_ms": round(ms_f, 5), "fused_TOPS": round(ops2 / (ms_f * 1e-3) / 1e12, 2),
+            "fused_step_ms_median": round(float(np.median(each_f)), 5),
+            "fused_parts_ms": {"act_up": round(per_f[0], 5), "up_gelu_quantize": round(per_f[1], 5),
+                               "down_linear": round(per_f[2], 5)},
+            "unfused_ms": round(ms_u, 5), "unfused_TOPS": round(ops2 / (ms_u * 1e-3) / 1e12, 2),
+            "unfused_parts_ms": {"act_up": round(per_u[0], 5), "up_linear": round(per_u[1], 5),
+                                 "gelu": round(per_u[2], 5), "act_down": round(per_u[3], 5),
+                                 "down_linear": round(per_u[4], 5)},
+            "speedup": round(ms_u / ms_f, 3),
+            "prepare_down_library_s": round(mlp_prep_s, 2),
+        }
+        log(f"[bench] mlp pair: fused {ms_f:.4f} ms (up+gelu+quant {per_f[1]:.4f}), unfused {ms_u:.4f} ms "
+            f"(up {per_u[1]:.4f}, gelu {per_u[2]:.4f}, act_down {per_u[3]:.4f}, down {per_u[4]:.4f})")
 
     if not args.no_w8a8:
         c8 = wl.CASES["w8a8_attn"]

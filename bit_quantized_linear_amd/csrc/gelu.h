@@ -32,18 +32,22 @@ namespace svdq {
 constexpr uint32_t kGeluExpLo = 118;  // exponent field of 2^-9
 constexpr uint32_t kGeluExpHi = 130;  // exponent field of 8 (|y| < 16)
 
+// The table's range holds nearly every value a layer produces: its lookup is
+// the straight-line path, the other rules one branch that lanes seldom take.
 __device__ __forceinline__ uint32_t gelu_bf16_bits(uint32_t b, const uint16_t *table) {
     const uint32_t sign = b & 0x8000u;
     const uint32_t e = (b >> 7) & 0xFFu;
-    if (e >= kGeluExpLo && e <= kGeluExpHi)
-        return table[(sign ? kGeluTableEntries / 2 : 0) + (e - kGeluExpLo) * 128u + (b & 0x7Fu)];
-    if (e < kGeluExpLo) {
-        if (e >= 2u) return b - 0x80u;  // y / 2
-        const uint32_t k = b & 0x7FFFu;
-        return sign | ((k + (sign ? 0u : 1u)) >> 1);
+    const uint32_t d = e - kGeluExpLo;  // wraps for e < kGeluExpLo
+    const bool mid = d <= kGeluExpHi - kGeluExpLo;
+    uint32_t r = table[mid ? (sign ? kGeluTableEntries / 2 : 0u) + d * 128u + (b & 0x7Fu) : 0u];
+    if (__builtin_expect(!mid, 0)) {
+        const uint32_t tiny = sign | (((b & 0x7FFFu) + (sign ? 0u : 1u)) >> 1);  // |y| < 2^-125
+        const uint32_t half = b - 0x80u;                                          // y / 2
+        const uint32_t special = b == 0x7F80u ? b : 0x7FC0u;                      // inf, NaN
+        const uint32_t big = e == 0xFFu ? special : (sign ? 0x8000u : b);         // |y| >= 16
+        r = e < kGeluExpLo ? (e < 2u ? tiny : half) : big;
     }
-    if (e == 0xFFu) return (b == 0x7F80u) ? b : 0x7FC0u;
-    return sign ? 0x8000u : b;
+    return r;
 }
 
 }  // namespace svdq

@@ -1,7 +1,8 @@
 // The MLP pair on the device, second half: the down-projection's low-rank T
 // from the per-column-tile partial sums the up-projection's MLP epilogue
-// wrote, and the GELU rule applied elementwise (a debug entry point that lets
-// the device's GELU be checked on every bf16 input).
+// wrote; and the same GELU rule as an elementwise pass (the entry point that
+// checks the device's GELU on every bf16 input, and the unfused pipeline's
+// GELU step in the benchmark).
 //
 // Source: "Hugging Face встроила Nunchaku в Diffusers..." (iitog.ru), method
 // paragraph (the 16-bit low-rank branch: T = X L1s rounded once to bf16) and
@@ -29,14 +30,36 @@ __global__ __launch_bounds__(256) void tpart_reduce_kernel(const float *__restri
     T[i] = (uint16_t)f32_to_bf16_bits(v);
 }
 
+// Elementwise GELU: each block loads the table into LDS once and handles
+// kGeluPerBlock elements; with 16-byte aligned pointers as 8-value vectors
+// (32 values per thread), else one value at a time.
+constexpr int kGeluPerBlock = 256 * 32;
+
 __global__ __launch_bounds__(256) void gelu_bf16_kernel(const uint16_t *__restrict__ y, uint16_t *__restrict__ g,
-                                                        int n) {
+                                                        int n, bool vec) {
     __shared__ __attribute__((aligned(16))) uint16_t tab[kGeluTableEntries];
     for (int i = threadIdx.x; i < kGeluTableEntries / 8; i += 256)
         reinterpret_cast<u32x4 *>(tab)[i] = reinterpret_cast<const u32x4 *>(kGeluTable)[i];
     __syncthreads();
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) g[i] = (uint16_t)gelu_bf16_bits(y[i], tab);
+    const int base = blockIdx.x * kGeluPerBlock;
+    if (vec) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = base + 8 * (k * 256 + (int)threadIdx.x);
+            if (e + 8 <= n) {
+                u32x4 w = *reinterpret_cast<const u32x4 *>(y + e);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w[j] = gelu_bf16_bits(w[j] & 0xFFFFu, tab) | (gelu_bf16_bits(w[j] >> 16, tab) << 16);
+                *reinterpret_cast<u32x4 *>(g + e) = w;
+            } else {
+                for (int i = e; i < min(e + 8, n); ++i) g[i] = (uint16_t)gelu_bf16_bits(y[i], tab);
+            }
+        }
+    } else {
+        for (int i = base + (int)threadIdx.x; i < min(base + kGeluPerBlock, n); i += 256)
+            g[i] = (uint16_t)gelu_bf16_bits(y[i], tab);
+    }
 }
 
 }  // namespace
@@ -51,7 +74,9 @@ hipError_t launch_tpart_reduce(const float *tpart, int parts, int M, int rank, u
 
 hipError_t launch_gelu_bf16(const uint16_t *y, uint16_t *g, int n, hipStream_t stream) {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(gelu_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, y, g, n);
+    const bool vec = (((uintptr_t)y | (uintptr_t)g) & 15u) == 0;
+    hipLaunchKernelGGL(gelu_bf16_kernel, dim3((unsigned)((n + kGeluPerBlock - 1) / kGeluPerBlock)), dim3(256), 0,
+                       stream, y, g, n, vec);
     return hipGetLastError();
 }
 

@@ -45,6 +45,26 @@ def test_device_gelu_on_every_bf16_input():
     assert same.all(), bits[~same][:10]
 
 
+def test_device_gelu_tails_and_unaligned_views():
+    """The elementwise pass on lengths that are not a multiple of its 8-value
+    vectors, and on views that are not 16-byte aligned (one value at a time)."""
+    t = H.torch()
+    bits = (np.arange(70001, dtype=np.uint32) * 2654435761 % 65536).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        want = mlp.gelu_bf16(sq.bf16_from_bits(bits))
+    y = H.dev(bits)
+    for lo, hi in ((0, 70001), (0, 8197), (1, 70001), (3, 1000)):
+        say("gelu view", lo, hi)
+        g = t.zeros(70001, dtype=t.int16, device="cuda")
+        b.svdq_debug_gelu_bf16(y[lo:hi], g[lo:hi])
+        t.cuda.synchronize()
+        got = sq.bf16_from_bits(H.host(g).view(np.uint16)[lo:hi])
+        w = want[lo:hi]
+        same = ((got == w) & (np.signbit(got) == np.signbit(w))) | (np.isnan(got) & np.isnan(w))
+        assert same.all()
+        assert not H.host(g)[:lo].any() and not H.host(g)[hi:].any()
+
+
 def pair_problem(M, K, N, N2, rank, rank_down, seed):
     """Up-projection [K -> N] on seeded X, down-projection [N -> N2] whose
     smoothing is calibrated on the oracle's GELU of the up output."""
