@@ -411,15 +411,17 @@ def main():
     sx = torch.empty((K // 64, M), dtype=torch.float32, device="cuda")
     T = torch.empty((M, r), dtype=torch.int16, device="cuda")
     Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    # the activation pass's workspace: K split across blocks at this batch
+    act_ws = torch.empty(max(16, b.svdq_act_workspace_bytes(M, K, r)), dtype=torch.uint8, device="cuda")
 
     def act6():
-        b.svdq_quantize_act(Xd, s_d, l1_d, qx6, sx, T, r, qfmt=b.QFMT_FP6)
+        b.svdq_quantize_act(Xd, s_d, l1_d, qx6, sx, T, r, qfmt=b.QFMT_FP6, workspace=act_ws)
 
     def gemm6():
         b.svdq_w4a4_linear(qx6, sx, T, qw6_d, sw_d, l2_d, b_d, Y, M, N, K, r, qfmt=b.QFMT_FP6)
 
     def act4():
-        b.svdq_quantize_act(Xd, s_d, l1_d, qx, sx, T, r, qfmt=b.QFMT_INT4)
+        b.svdq_quantize_act(Xd, s_d, l1_d, qx, sx, T, r, qfmt=b.QFMT_INT4, workspace=act_ws)
 
     def gemm4():
         b.svdq_w4a4_linear(qx, sx, T, qw_d, sw_d, l2_d, b_d, Y, M, N, K, r, qfmt=b.QFMT_INT4)
@@ -498,7 +500,7 @@ def main():
         mux = torch.empty((K // 32, b.svdq_mx_scale_ld(M)), dtype=torch.uint8, device="cuda")
 
         def actmx():
-            b.svdq_mx_quantize_act(Xd, s_d, l1_d, mqx, mux, T, r)
+            b.svdq_mx_quantize_act(Xd, s_d, l1_d, mqx, mux, T, r, workspace=act_ws)
 
         def gemmmx():
             b.svdq_mx_linear(mqx, mux, T, mqw, muw, l2_d, b_d, Y, M, N, K, r)
@@ -549,12 +551,13 @@ def main():
         Td = torch.empty((M, rd), dtype=torch.int16, device="cuda")
         Yd = torch.empty((M, Nd), dtype=torch.int16, device="cuda")
         ws = torch.empty(b.svdq_mlp_workspace_bytes(M, Kd, rd), dtype=torch.uint8, device="cuda")
+        act_ws_d = torch.empty(max(16, b.svdq_act_workspace_bytes(M, Kd, rd)), dtype=torch.uint8, device="cuda")
 
         def gelu():
             b.svdq_debug_gelu_bf16(Y, G)
 
         def act_d():
-            b.svdq_quantize_act(G, sd_d, l1d_d, qxd, sxd, Td, rd, qfmt=b.QFMT_FP6)
+            b.svdq_quantize_act(G, sd_d, l1d_d, qxd, sxd, Td, rd, qfmt=b.QFMT_FP6, workspace=act_ws_d)
 
         def fused():
             b.svdq_w4a4_linear_gelu_quantize(qx6, sx, T, qw6_d, sw_d, l2_d, b_d, M, N, K, r, sd_d, l1d_d, rd,

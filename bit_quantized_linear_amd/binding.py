@@ -42,7 +42,8 @@ SIGNATURES = {
     "svdq_prepare_residual": (_i, [_vp, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp]),
     "w8a8_prepare_weights": (_i, [_vp, _i, _i, _vp, _vp]),
     "svdq_channel_absmax": (_i, [_vp, _i, _i, _vp, _vp]),
-    "svdq_quantize_act": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "svdq_act_workspace_bytes": (_sz, [_i, _i, _i]),
+    "svdq_quantize_act": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "svdq_w4a4_linear": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
     "svdq_mlp_workspace_bytes": (_sz, [_i, _i, _i]),
     "svdq_w4a4_linear_gelu_quantize": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _i,
@@ -52,7 +53,7 @@ SIGNATURES = {
     "w8a8_linear": (_i, [_vp, _vp, _f, _vp, _i, _i, _i, _vp, _sz, _vp, _vp]),
     "svdq_mx_scale_ld": (_sz, [_i]),
     "svdq_mx_prepare_residual": (_i, [_vp, _i, _i, _vp, _vp, _vp, _i, _vp, _vp]),
-    "svdq_mx_quantize_act": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "svdq_mx_quantize_act": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "svdq_mx_linear": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _vp]),
     "w4a16_weight_bytes": (_sz, [_i, _i]),
     "w4a16_prepare_weights": (_i, [_vp, _i, _i, _i, _vp]),
@@ -253,11 +254,21 @@ def svdq_channel_absmax(X, absmax, stream=None):
     _check("svdq_channel_absmax", st)
 
 
-def svdq_quantize_act(X, smooth, l1t, qx, sx, T, rank, group=GROUP, qfmt=QFMT_INT4, stream=None):
+def svdq_act_workspace_bytes(M, K, rank) -> int:
+    return int(lib().svdq_act_workspace_bytes(M, K, rank))
+
+
+def _ws(workspace):
+    return (None, 0) if workspace is None else (_dev_ptr(workspace), workspace.numel() * workspace.element_size())
+
+
+def svdq_quantize_act(X, smooth, l1t, qx, sx, T, rank, group=GROUP, qfmt=QFMT_INT4, workspace=None,
+                      stream=None):
     M, K = X.shape
+    wp, wb = _ws(workspace)
     st = lib().svdq_quantize_act(_dev_ptr(X, 2), _dev_ptr(smooth, 4), _dev_ptr(l1t, 2), M, K, rank,
                                  group, qfmt, _dev_ptr(qx, 1), _dev_ptr(sx, 4), _dev_ptr(T, 2),
-                                 _stream(stream))
+                                 wp, wb, _stream(stream))
     _check("svdq_quantize_act", st)
 
 
@@ -304,10 +315,11 @@ def w8a8_linear(X, qw, sw, bias, workspace, Y, stream=None):
     _check("w8a8_linear", st)
 
 
-def svdq_mx_quantize_act(X, smooth, l1t, qx, ux, T, rank, stream=None):
+def svdq_mx_quantize_act(X, smooth, l1t, qx, ux, T, rank, workspace=None, stream=None):
     M, K = X.shape
+    wp, wb = _ws(workspace)
     st = lib().svdq_mx_quantize_act(_dev_ptr(X, 2), _dev_ptr(smooth, 4), _dev_ptr(l1t, 2), M, K, rank,
-                                    _dev_ptr(qx, 1), _dev_ptr(ux, 1), _dev_ptr(T, 2), _stream(stream))
+                                    _dev_ptr(qx, 1), _dev_ptr(ux, 1), _dev_ptr(T, 2), wp, wb, _stream(stream))
     _check("svdq_mx_quantize_act", st)
 
 

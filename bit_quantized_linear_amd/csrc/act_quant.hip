@@ -20,14 +20,17 @@ namespace {
 constexpr int kActWaves = 8;   // waves per block; they split the K groups
 constexpr int kActRows = 16;   // token rows per block (one 16x16 MFMA row tile)
 
-// One block owns 16 token rows and walks all K groups; wave w takes groups
-// w, w + 8, ... . Lane l holds row (l % 16) and the 16 consecutive channels
+// One block owns 16 token rows and a range of K groups (all of K, or a
+// 1 / gridDim.y share when the launcher splits K across blocks so that
+// small batches still fill the chip); wave w takes the range's groups w,
+// w + 8, ... . Lane l holds row (l % 16) and the 16 consecutive channels
 // [64 g + 16 (l / 16), +16) of group g: two 128-bit loads of X. The four
 // lanes of a row meet through two cross-lane max steps for the group absmax.
 // For the branch, the lane's 16 channels feed two 16x16x32 bf16 MFMAs per
 // rank tile (8 channels each); B comes from l1t with the same channel
 // mapping. The 8 waves' fp32 partial T tiles are summed in wave order through
-// LDS, so T is deterministic.
+// LDS; with K split, each block stores its fp32 partial and a second kernel
+// sums the partials in K order, so T is deterministic either way.
 // E2M1 code of q (|q| < 8): nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to
 // the even mantissa (rintf rounds half to even, and in each binade the even
 // multiple of the quantum is the even mantissa), saturating at 6; bit 3 is
@@ -57,7 +60,8 @@ template <int kFmt, int RT>
 __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ smooth,
     const uint16_t *__restrict__ l1t, int M, int K, int rank,
-    uint8_t *__restrict__ qx, void *__restrict__ sx_out, int sx_ld, uint16_t *__restrict__ T) {
+    uint8_t *__restrict__ qx, void *__restrict__ sx_out, int sx_ld, uint16_t *__restrict__ T,
+    float *__restrict__ tpart) {
     constexpr int kRT = RT > 0 ? RT : 1;  // rank tiles held (rank / 16, at least one array slot)
     __shared__ float red[kActWaves][kActRows][16 * kRT];
     __shared__ double rcp[kActWaves][SVDQ_GROUP];  // per wave: 1/s of its current group's channels
@@ -70,6 +74,7 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
     const int m = m0 + row;
     const bool row_ok = m < M;
     const int G = K / SVDQ_GROUP;
+    const int g_lo = (int)(blockIdx.y * G / gridDim.y), g_hi = (int)((blockIdx.y + 1) * G / gridDim.y);
     constexpr int rtiles = RT;
 
     f32x4 tacc[kRT];
@@ -81,7 +86,7 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
     u32x4 nxa = {0u, 0u, 0u, 0u}, nxb = {0u, 0u, 0u, 0u};
     float ns = 1.0f;
     auto load_next = [&](int g) {
-        if (g < G) {
+        if (g < g_hi) {
             if (row_ok) {
                 const u32x4 *p = reinterpret_cast<const u32x4 *>(X + (size_t)m * K + g * SVDQ_GROUP + quad * 16);
                 nxa = p[0];
@@ -90,8 +95,8 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
             ns = smooth[g * SVDQ_GROUP + lane];
         }
     };
-    load_next(wave);
-    for (int g = wave; g < G; g += kActWaves) {
+    load_next(g_lo + wave);
+    for (int g = g_lo + wave; g < g_hi; g += kActWaves) {
         const int kb = g * SVDQ_GROUP + quad * 16;
         const u32x4 xa = nxa, xb = nxb;
         const float sg = ns;
@@ -249,7 +254,12 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
         float v = 0.0f;
 #pragma unroll
         for (int w = 0; w < kActWaves; ++w) v += red[w][r][j];
-        if (m0 + r < M) T[(size_t)(m0 + r) * rank + j] = (uint16_t)f32_to_bf16_bits(v);
+        if (m0 + r < M) {
+            if (gridDim.y == 1)
+                T[(size_t)(m0 + r) * rank + j] = (uint16_t)f32_to_bf16_bits(v);
+            else
+                tpart[((size_t)blockIdx.y * M + m0 + r) * rank + j] = v;
+        }
     }
 }
 
@@ -295,42 +305,72 @@ __global__ __launch_bounds__(256) void channel_absmax_kernel(const uint16_t *__r
 template <int RT>
 static void launch_act_rt(dim3 grid, hipStream_t stream, int fmt, const uint16_t *X, const float *smooth,
                           const uint16_t *l1t, int M, int K, int rank, uint8_t *qx, void *sx, int sx_ld,
-                          uint16_t *T) {
+                          uint16_t *T, float *tpart) {
     if (fmt == kFp6)
         hipLaunchKernelGGL((quantize_act_kernel<kFp6, RT>), grid, dim3(kActWaves * 64), 0, stream, X, smooth,
-                           l1t, M, K, rank, qx, sx, sx_ld, T);
+                           l1t, M, K, rank, qx, sx, sx_ld, T, tpart);
     else if (fmt == kMx)
         hipLaunchKernelGGL((quantize_act_kernel<kMx, RT>), grid, dim3(kActWaves * 64), 0, stream, X, smooth,
-                           l1t, M, K, rank, qx, sx, sx_ld, T);
+                           l1t, M, K, rank, qx, sx, sx_ld, T, tpart);
     else
         hipLaunchKernelGGL((quantize_act_kernel<kInt4, RT>), grid, dim3(kActWaves * 64), 0, stream, X, smooth,
-                           l1t, M, K, rank, qx, sx, sx_ld, T);
+                           l1t, M, K, rank, qx, sx, sx_ld, T, tpart);
 }
 
-static hipError_t launch_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M, int K,
-                             int rank, int fmt, uint8_t *qx, void *sx, int sx_ld, uint16_t *T,
-                             hipStream_t stream) {
-    const dim3 grid((M + kActRows - 1) / kActRows);
-    switch (rank / 16) {  // rank % 16 == 0 and rank <= 64 are checked by the caller
-        case 0: launch_act_rt<0>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T); break;
-        case 1: launch_act_rt<1>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T); break;
-        case 2: launch_act_rt<2>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T); break;
-        case 3: launch_act_rt<3>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T); break;
-        default: launch_act_rt<4>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T); break;
+// How many blocks share the K range of one 16-row tile: the largest divisor
+// d of the group count that leaves every wave whole groups (G / d a multiple
+// of 8, the waves per block) and keeps the grid within 4 blocks per compute
+// unit, or within 8 when each block still has 4 groups per wave. More parts
+// balance the grid better but add T partials to write and sum (measured at
+// M = 4608: 3 parts best at K = 3072, 6 at K = 12288).
+int act_k_parts(int M, int K) {
+    const int64_t blocks = (M + kActRows - 1) / kActRows;
+    const int G = K / SVDQ_GROUP;
+    int kp = 1;
+    for (int d = 2; d <= G / kActWaves; ++d) {
+        if (G % d != 0 || (G / d) % kActWaves != 0) continue;
+        if (blocks * d <= 1024 || (blocks * d <= 2048 && G / d >= 4 * kActWaves)) kp = d;
     }
-    return hipGetLastError();
+    return kp;
+}
+
+size_t act_workspace_size(int M, int K, int rank) {
+    if (M <= 0 || K <= 0 || rank <= 0) return 0;
+    const int kp = act_k_parts(M, K);
+    return kp > 1 ? (size_t)kp * (size_t)M * (size_t)rank * sizeof(float) : 0;
+}
+
+// Without a workspace for T's partials the K range is split only when there
+// is no T (rank 0).
+static hipError_t launch_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M, int K,
+                             int rank, int fmt, uint8_t *qx, void *sx, int sx_ld, uint16_t *T, float *workspace,
+                      hipStream_t stream) {
+    const int kp = (rank == 0 || workspace) ? act_k_parts(M, K) : 1;
+    float *tpart = kp > 1 && rank ? workspace : nullptr;
+    const dim3 grid((M + kActRows - 1) / kActRows, kp);
+    switch (rank / 16) {  // rank % 16 == 0 and rank <= 64 are checked by the caller
+        case 0: launch_act_rt<0>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T, tpart); break;
+        case 1: launch_act_rt<1>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T, tpart); break;
+        case 2: launch_act_rt<2>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T, tpart); break;
+        case 3: launch_act_rt<3>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T, tpart); break;
+        default: launch_act_rt<4>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T, tpart); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !tpart) return e;
+    return launch_tpart_reduce(tpart, kp, M, rank, T, stream);
 }
 
 hipError_t launch_quantize_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M,
                                int K, int rank, int qfmt, uint8_t *qx, float *sx, uint16_t *T,
-                               hipStream_t stream) {
-    return launch_act(X, smooth, l1t, M, K, rank, qfmt == SVDQ_QFMT_FP6 ? kFp6 : kInt4, qx, sx, M, T, stream);
+                               float *workspace, hipStream_t stream) {
+    return launch_act(X, smooth, l1t, M, K, rank, qfmt == SVDQ_QFMT_FP6 ? kFp6 : kInt4, qx, sx, M, T, workspace,
+                      stream);
 }
 
 hipError_t launch_mx_quantize_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M,
-                                  int K, int rank, uint8_t *qx, uint8_t *ux, uint16_t *T,
+                                  int K, int rank, uint8_t *qx, uint8_t *ux, uint16_t *T, float *workspace,
                                   hipStream_t stream) {
-    return launch_act(X, smooth, l1t, M, K, rank, kMx, qx, ux, (int)mx_scale_ld(M), T, stream);
+    return launch_act(X, smooth, l1t, M, K, rank, kMx, qx, ux, (int)mx_scale_ld(M), T, workspace, stream);
 }
 
 hipError_t launch_channel_absmax(const uint16_t *X, int M, int K, float *absmax,

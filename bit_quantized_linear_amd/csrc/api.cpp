@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 constexpr int kMaxDevices = 64;
 
 std::mutex g_mutex;
@@ -218,23 +218,30 @@ svdq_status svdq_channel_absmax(const uint16_t *X, int M, int K, float *absmax, 
     return launched(svdq::launch_channel_absmax(X, M, K, absmax, (hipStream_t)stream));
 }
 
+size_t svdq_act_workspace_bytes(int M, int K, int rank) {
+    if (M < 0 || K <= 0 || K % SVDQ_GROUP || rank < 0) return 0;
+    return svdq::act_workspace_size(M, K, rank);
+}
+
 svdq_status svdq_quantize_act(const uint16_t *X, const float *smooth,
                               const uint16_t *l1t, int M, int K, int rank,
                               int group, int qfmt, uint8_t *qx, float *sx,
-                              uint16_t *T, void *stream) {
+                              uint16_t *T, void *workspace, size_t workspace_bytes, void *stream) {
     svdq_status st = check_w4a4_shape(M, K, rank, group);
     if (st != SVDQ_OK) return st;
     if (qfmt != SVDQ_QFMT_INT4 && qfmt != SVDQ_QFMT_FP6) return SVDQ_ERR_INVALID_ARGUMENT;
     if (!smooth || (M > 0 && (!X || !qx || !sx))) return SVDQ_ERR_INVALID_ARGUMENT;
     if (rank > 0 && (!l1t || (M > 0 && !T))) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (workspace && workspace_bytes < svdq::act_workspace_size(M, K, rank)) return SVDQ_ERR_INVALID_ARGUMENT;
     if (!aligned16(X) || !aligned16(smooth) || !aligned16(l1t) || !aligned16(qx) ||
-        !aligned16(sx) || !aligned16(T))
+        !aligned16(sx) || !aligned16(T) || !aligned16(workspace))
         return SVDQ_ERR_MISALIGNED;
     st = current_device_ok();
     if (st != SVDQ_OK) return st;
     if (M == 0) return SVDQ_OK;
     return launched(svdq::launch_quantize_act(X, smooth, rank ? l1t : nullptr, M, K, rank, qfmt, qx, sx,
-                                              rank ? T : nullptr, (hipStream_t)stream));
+                                              rank ? T : nullptr, static_cast<float *>(workspace),
+                                              (hipStream_t)stream));
 }
 
 size_t svdq_mlp_workspace_bytes(int M, int N, int rank_down) {
@@ -368,13 +375,15 @@ svdq_status w4a16_linear(const uint16_t *X, const uint8_t *packed, const uint16_
 }
 
 svdq_status svdq_mx_quantize_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M,
-                                 int K, int rank, uint8_t *qx, uint8_t *ux, uint16_t *T, void *stream) {
+                                 int K, int rank, uint8_t *qx, uint8_t *ux, uint16_t *T, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
     svdq_status st = check_w4a4_shape(M, K, rank, SVDQ_GROUP);
     if (st != SVDQ_OK) return st;
     if (!smooth || (M > 0 && (!X || !qx || !ux))) return SVDQ_ERR_INVALID_ARGUMENT;
     if (rank > 0 && (!l1t || (M > 0 && !T))) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (workspace && workspace_bytes < svdq::act_workspace_size(M, K, rank)) return SVDQ_ERR_INVALID_ARGUMENT;
     if (!aligned16(X) || !aligned16(smooth) || !aligned16(l1t) || !aligned16(qx) || !aligned16(ux) ||
-        !aligned16(T))
+        !aligned16(T) || !aligned16(workspace))
         return SVDQ_ERR_MISALIGNED;
     if (!fits_buffer(M, K / 2) || !fits_buffer(K / 32, (int64_t)svdq::mx_scale_ld(M)))
         return SVDQ_ERR_UNSUPPORTED_SHAPE;
@@ -382,7 +391,8 @@ svdq_status svdq_mx_quantize_act(const uint16_t *X, const float *smooth, const u
     if (st != SVDQ_OK) return st;
     if (M == 0) return SVDQ_OK;
     return launched(svdq::launch_mx_quantize_act(X, smooth, rank ? l1t : nullptr, M, K, rank, qx, ux,
-                                                 rank ? T : nullptr, (hipStream_t)stream));
+                                                 rank ? T : nullptr, static_cast<float *>(workspace),
+                                                 (hipStream_t)stream));
 }
 
 svdq_status svdq_mx_linear(const uint8_t *qx, const uint8_t *ux, const uint16_t *T, const uint8_t *qw,

@@ -36,10 +36,14 @@ bool all_finite_bf16(const uint16_t *p, int64_t n);
 // Arguments are validated by the caller; launchers only pick a grid and launch.
 hipError_t launch_channel_absmax(const uint16_t *X, int M, int K, float *absmax,
                                  hipStream_t stream);
+// activation passes: workspace (nullable) holds act_workspace_size(M, K,
+// rank) bytes for T's fp32 partials when K is split across blocks
+int act_k_parts(int M, int K);
+size_t act_workspace_size(int M, int K, int rank);
 hipError_t launch_quantize_act(const uint16_t *X, const float *smooth,
                                const uint16_t *l1t, int M, int K, int rank,
                                int qfmt, uint8_t *qx, float *sx, uint16_t *T,
-                               hipStream_t stream);
+                               float *workspace, hipStream_t stream);
 hipError_t launch_w4a4_linear(const uint8_t *qx, const float *sx,
                               const uint16_t *T, const uint8_t *qw,
                               const float *sw, const uint16_t *l2t,
@@ -81,7 +85,7 @@ hipError_t launch_w8a8_acc(const int8_t *qx, const int8_t *qw, int M, int N,
 size_t w8a8_workspace_size(int M, int K);
 int w4a16_rows_per_block(int M, int K);
 hipError_t launch_mx_quantize_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M,
-                                  int K, int rank, uint8_t *qx, uint8_t *ux, uint16_t *T,
+                                  int K, int rank, uint8_t *qx, uint8_t *ux, uint16_t *T, float *workspace,
                                   hipStream_t stream);
 hipError_t launch_mx_linear(const uint8_t *qx, const uint8_t *ux, const uint16_t *T, const uint8_t *qw,
                             const uint8_t *uw, const uint16_t *l2t, const uint16_t *bias, int M, int N, int K,

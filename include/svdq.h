@@ -262,6 +262,11 @@ svdq_status svdq_repack_codes(const uint8_t *q, int rows, int K, int qfmt,
 svdq_status svdq_channel_absmax(const uint16_t *X, int M, int K, float *absmax,
                                 void *stream);
 
+/* Bytes of the optional device workspace of svdq_quantize_act and
+ * svdq_mx_quantize_act for an [M, K] input at this rank (0 when the pass
+ * needs none). */
+size_t svdq_act_workspace_bytes(int M, int K, int rank);
+
 /* Fused activation quantization -- one pass over X [HF-SVDQ method]:
  *   X_hat = fp32(X / s_k)   (IEEE fp32 division, round to nearest even);
  *   per row m and K-group g: A = max |X_hat|, sx[g, m] = fp32(A / 7),
@@ -274,13 +279,20 @@ svdq_status svdq_channel_absmax(const uint16_t *X, int M, int K, float *absmax,
  * Out: qx [M, svdq_qrow_bytes(K, qfmt)]; sx [K/64, M] fp32; T [M, rank] bf16 (NULL if
  *      rank 0). M >= 0 (M == 0 launches nothing), K % 64 == 0,
  *      rank % 16 == 0, rank <= 64, group == 64.
- * Deterministic: T's partial sums are combined in a fixed order.
+ * Workspace: NULL, or device memory of at least svdq_act_workspace_bytes(M,
+ *      K, rank) bytes owned by the caller (not read before it is written):
+ *      with it the pass splits K across blocks (fp32 partial sums of T,
+ *      combined by a second kernel), which fills the GPU when M is small.
+ *      A non-NULL workspace that is too small is INVALID_ARGUMENT.
+ * Deterministic: T's partial sums are combined in a fixed order (which
+ *      depends only on M, K and whether a workspace is given).
  * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, MISALIGNED, UNSUPPORTED_DEVICE,
  *      HIP. */
 svdq_status svdq_quantize_act(const uint16_t *X, const float *smooth,
                               const uint16_t *l1t, int M, int K, int rank,
                               int group, int qfmt, uint8_t *qx, float *sx,
-                              uint16_t *T, void *stream);
+                              uint16_t *T, void *workspace, size_t workspace_bytes,
+                              void *stream);
 
 /* The W4A4 linear with fused low-rank up-projection and bias
  * [HF-SVDQ method and "Nunchaku Lite" paragraph]:
@@ -371,12 +383,13 @@ svdq_status w8a8_linear(const uint16_t *X, const int8_t *qw, float sw,
  * Out: qx: MX code container of M rows; ux [K/32][ld(M)] (16-byte aligned);
  *      T [M, rank] bf16 (NULL if rank 0). K % 64 == 0, rank % 16 == 0,
  *      rank <= 64; M == 0 launches nothing.
+ * Workspace: as svdq_quantize_act (svdq_act_workspace_bytes).
  * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, MISALIGNED, UNSUPPORTED_DEVICE,
  *      HIP. */
 svdq_status svdq_mx_quantize_act(const uint16_t *X, const float *smooth,
                                  const uint16_t *l1t, int M, int K, int rank,
                                  uint8_t *qx, uint8_t *ux, uint16_t *T,
-                                 void *stream);
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /* The MXFP4 linear with fused low-rank up-projection and bias:
  *   acc[m, n] = sum_b 2^(ex[b, m] + ew[b, n]) sum_{k in b} e2m1(qx) e2m1(qw)

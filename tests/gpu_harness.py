@@ -88,7 +88,16 @@ def weights_bytes(prep, abi, qfmt):
     return abi["qw"] if qfmt == b.QFMT_INT4 else pack_codes(np.asarray(prep["qw"]).T, qfmt)
 
 
-def run_quantize_act(Xbits, abi, rank, qfmt=b.QFMT_INT4):
+def act_workspace(M, K, rank):
+    """The activation pass's optional workspace (None when it needs none)."""
+    t = torch()
+    n = b.svdq_act_workspace_bytes(M, K, rank)
+    return t.empty(n, dtype=t.uint8, device="cuda") if n else None
+
+
+def run_quantize_act(Xbits, abi, rank, qfmt=b.QFMT_INT4, split=True):
+    """The activation pass as the bench runs it (with its workspace: K split
+    across blocks where that fills the GPU better), or without (split=False)."""
     t = torch()
     M, K = Xbits.shape
     Xd = dev(Xbits)
@@ -96,7 +105,8 @@ def run_quantize_act(Xbits, abi, rank, qfmt=b.QFMT_INT4):
     sx = t.empty((K // 64, M), dtype=t.float32, device="cuda")
     T = t.empty((M, max(rank, 1)), dtype=t.int16, device="cuda") if rank else None
     l1t = dev(abi["l1t"]) if rank else None
-    b.svdq_quantize_act(Xd, dev(abi["s"]), l1t, qx, sx, T, rank, qfmt=qfmt)
+    b.svdq_quantize_act(Xd, dev(abi["s"]), l1t, qx, sx, T, rank, qfmt=qfmt,
+                        workspace=act_workspace(M, K, rank) if split else None)
     t.cuda.synchronize()
     return qx, sx, T
 

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert b.svdq_version() == 6
+    assert b.svdq_version() == 7
     for s in range(7):
         assert b.status_string(s)
     assert "unknown" in b.status_string(99)
@@ -55,7 +55,7 @@ def test_arch_override_fails_closed_before_launch():
     lib = b.lib()
     b.svdq_debug_set_arch_override("gfx942")
     try:
-        st = lib.svdq_quantize_act(FAKE, FAKE, FAKE, 16, 128, 16, 64, 0, FAKE, FAKE, FAKE, None)
+        st = lib.svdq_quantize_act(FAKE, FAKE, FAKE, 16, 128, 16, 64, 0, FAKE, FAKE, FAKE, None, 0, None)
         assert st == b.SVDQ_ERR_UNSUPPORTED_DEVICE
         st = lib.svdq_w4a4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 64, 128, 16, 64, 1,
                                   FAKE, b.SVDQ_BF16, None)
@@ -77,17 +77,17 @@ def test_arch_override_fails_closed_before_launch():
 ])
 def test_quantize_act_shape_checks(args, expected):
     M, K, rank, group = args
-    st = b.lib().svdq_quantize_act(FAKE, FAKE, FAKE, M, K, rank, group, 0, FAKE, FAKE, FAKE, None)
+    st = b.lib().svdq_quantize_act(FAKE, FAKE, FAKE, M, K, rank, group, 0, FAKE, FAKE, FAKE, None, 0, None)
     assert st == expected
 
 
 def test_null_and_misaligned_pointers_rejected():
     lib = b.lib()
-    assert lib.svdq_quantize_act(None, FAKE, FAKE, 16, 128, 16, 64, 0, FAKE, FAKE, FAKE, None) == \
+    assert lib.svdq_quantize_act(None, FAKE, FAKE, 16, 128, 16, 64, 0, FAKE, FAKE, FAKE, None, 0, None) == \
         b.SVDQ_ERR_INVALID_ARGUMENT
-    assert lib.svdq_quantize_act(MISALIGNED, FAKE, FAKE, 16, 128, 16, 64, 0, FAKE, FAKE, FAKE, None) == \
+    assert lib.svdq_quantize_act(MISALIGNED, FAKE, FAKE, 16, 128, 16, 64, 0, FAKE, FAKE, FAKE, None, 0, None) == \
         b.SVDQ_ERR_MISALIGNED
-    assert lib.svdq_quantize_act(FAKE, FAKE, FAKE, 16, 128, 16, 64, 2, FAKE, FAKE, FAKE, None) == \
+    assert lib.svdq_quantize_act(FAKE, FAKE, FAKE, 16, 128, 16, 64, 2, FAKE, FAKE, FAKE, None, 0, None) == \
         b.SVDQ_ERR_INVALID_ARGUMENT  # unknown container
     assert lib.svdq_w4a4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 60, 128, 16, 64, 0, FAKE,
                                 b.SVDQ_BF16, None) == b.SVDQ_ERR_UNSUPPORTED_SHAPE  # N % 8
@@ -288,3 +288,17 @@ def test_mlp_pair_entry_point_fails_closed():
         assert b.lib().svdq_debug_gelu_bf16(FAKE, FAKE, 4, None) == b.SVDQ_ERR_UNSUPPORTED_DEVICE
     finally:
         b.svdq_debug_set_arch_override(None)
+
+
+def test_act_workspace_is_optional_but_checked():
+    lib = b.lib()
+    need = b.svdq_act_workspace_bytes(4608, 3072, 32)
+    assert need == 3 * 4608 * 32 * 4  # K split three ways at this shape
+    assert b.svdq_act_workspace_bytes(4608, 12288, 32) == 6 * 4608 * 32 * 4
+    assert b.svdq_act_workspace_bytes(4608, 3072, 0) == 0
+    assert b.svdq_act_workspace_bytes(4608, 100, 32) == 0
+    args = (FAKE, FAKE, FAKE, 4608, 3072, 32, 64, 1, FAKE, FAKE, FAKE)
+    assert lib.svdq_quantize_act(*args, FAKE, need - 4, None) == b.SVDQ_ERR_INVALID_ARGUMENT
+    assert lib.svdq_quantize_act(*args, MISALIGNED, need, None) == b.SVDQ_ERR_MISALIGNED
+    assert lib.svdq_mx_quantize_act(FAKE, FAKE, FAKE, 4608, 3072, 32, FAKE, FAKE, FAKE, FAKE, 16, None) == \
+        b.SVDQ_ERR_INVALID_ARGUMENT

@@ -55,14 +55,15 @@ def problem(M, K, N, rank, seed, outliers=(), bias=True):
     return Xb, Xv, prep, bb
 
 
-def run_act(Xb, prep, rank):
+def run_act(Xb, prep, rank, split=True):
     t = H.torch()
     M, K = Xb.shape
     qx = t.empty((M, K // 2), dtype=t.uint8, device="cuda")
     ux = t.empty((K // 32, scale_ld(M)), dtype=t.uint8, device="cuda")
     T = t.empty((M, max(rank, 1)), dtype=t.int16, device="cuda") if rank else None
     l1t = H.dev(sq.bf16_bits(np.asarray(prep["L1s"]).T)) if rank else None
-    b.svdq_mx_quantize_act(H.dev(Xb), H.dev(prep["s"].astype(np.float32)), l1t, qx, ux, T, rank)
+    b.svdq_mx_quantize_act(H.dev(Xb), H.dev(prep["s"].astype(np.float32)), l1t, qx, ux, T, rank,
+                           workspace=H.act_workspace(M, K, rank) if split else None)
     t.cuda.synchronize()
     return qx, ux, T
 
@@ -191,3 +192,20 @@ def test_mx_linear_mlp_up_sampled_rows():
     Y = run_linear(qx, ux, T, prep, bias["bits"], case.M, case.N, case.K, case.rank)
     rows = np.array([0, 1, 127, 128, 2047, 4095, 4096, 4607])
     check_y(Y, Xv, prep, bias["bits"], case.rank, rows=rows)
+
+
+@pytest.mark.parametrize("M,K,rank", [(64, 1024, 32), (130, 3072, 16)])
+def test_mx_act_split_and_single_pass_agree(M, K, rank):
+    """With its workspace the pass splits K across blocks (2 and 6 ways at
+    these shapes); codes and scales are identical to the single pass and T
+    is within the same bound of the oracle on both paths."""
+    say("mx act split", M, K, rank)
+    Xb, Xv, prep, _ = problem(M, K, 64, rank, seed=M + K, outliers=(3, K - 7))
+    assert b.svdq_act_workspace_bytes(M, K, rank) > 0
+    a = run_act(Xb, prep, rank, split=True)
+    c = run_act(Xb, prep, rank, split=False)
+    # the scale matrix's padding columns (rows M..ld) are never written
+    assert np.array_equal(H.host(a[0]), H.host(c[0]))
+    assert np.array_equal(H.host(a[1])[:, :M], H.host(c[1])[:, :M])
+    for r in (a, c):
+        check_act(*r, Xv, prep, rank)

@@ -65,6 +65,24 @@ def check_output(y, ref):
 # ------------------------------------------------------------ act quant --
 
 @pytest.mark.parametrize("qfmt", H.FORMATS, ids=H.FORMAT_IDS)
+@pytest.mark.parametrize("M,K,rank", [(64, 1024, 32), (130, 3072, 16), (300, 512, 0)])
+def test_quantize_act_split_and_single_pass_agree(M, K, rank, qfmt):
+    """With its workspace the pass splits K across blocks; codes and scales
+    are identical to the single pass, and T is within the same bound of the
+    oracle on both paths (the split changes only T's fp32 summation order)."""
+    say("quantize_act split", M, K, rank, qfmt)
+    p = H.make_problem(M, K, 64, rank, seed=M + 1, outliers=(3, K - 5))
+    a = H.run_quantize_act(p["X"]["bits"], p["abi"], rank, qfmt, split=True)
+    c = H.run_quantize_act(p["X"]["bits"], p["abi"], rank, qfmt, split=False)
+    cx, csx = sq.quantize_activations(p["X"]["values"], p["prep"]["s"])
+    for r in (a, c):
+        assert np.array_equal(H.host(r[0]), H.pack_codes(cx, qfmt))
+        assert np.array_equal(H.host(r[1]), csx)
+        if rank:
+            check_T(r[2], sq.lowrank_down(p["X"]["values"], p["prep"]["L1s"]), p["X"]["values"], p["prep"]["L1s"])
+
+
+@pytest.mark.parametrize("qfmt", H.FORMATS, ids=H.FORMAT_IDS)
 @pytest.mark.parametrize("shape", [(64, 256, 16), (77, 320, 32), (1, 64, 16), (130, 128, 0), (33, 192, 64)])
 def test_quantize_act_small(shape, qfmt):
     M, K, rank = shape
