@@ -77,29 +77,33 @@ __device__ __forceinline__ void unpack_int4x16(uint32_t a, uint32_t b, uint32_t 
 }
 
 // ---- Output tile store through LDS -----------------------------------------
-// A block's 128 (n) x 128 (m) output tile, held by 2 x 2 waves (wn, wm) as
-// 2 x 2 32x32 fp32 MFMA tiles each (lane: column m = wm 64 + im 32 + l % 32,
-// rows n = wn 64 + in 32 + 8 qq + 4 (l / 32) + t), plus bias[n], rounded to
-// bf16 (nearest even) or kept fp32, stored to Y [M][N] (row m, N contiguous).
-// Stored straight from the MFMA layout, one instruction would write 16 bytes
-// into each of 32 rows; staged through LDS instead, in two passes of 64
-// tokens (the waves of one wm row write, everyone stores), each 16 lanes
-// write one contiguous row segment of 256 (bf16) or 512 (fp32) bytes.
+// A block's (64 WN) (n) x 128 (m) output tile, held by WN x 2 waves (wn, wm)
+// as 2 x 2 32x32 fp32 MFMA tiles each (lane: column m = wm 64 + im 32 +
+// l % 32, rows n = wn 64 + in 32 + 8 qq + 4 (l / 32) + t), plus bias[n],
+// rounded to bf16 (nearest even) or kept fp32, stored to Y [M][N] (row m, N
+// contiguous). Stored straight from the MFMA layout, one instruction would
+// write 16 bytes into each of 32 rows; staged through LDS instead, in two
+// passes of 64 tokens (the waves of one wm row write, everyone stores), each
+// 16-byte piece of a row segment of 128 WN (bf16) or 256 WN (fp32) bytes is
+// stored by one lane, consecutive lanes along the row.
 // Needs N % 8 == 0 and Y 16-byte aligned (16-byte pieces never straddle the
-// end of a row), `lds` >= 64 x 528 bytes not in use by anyone, and all 256
-// threads of the block (it synchronizes).
-constexpr int kTileStoreLdsBytes = 64 * 528;
+// end of a row), `lds` >= tile_store_lds_bytes(WN) bytes not in use by
+// anyone, and all 128 WN threads of the block (it synchronizes).
+constexpr int tile_store_lds_bytes(int WN) { return 64 * (256 * WN + 16); }
+constexpr int kTileStoreLdsBytes = tile_store_lds_bytes(2);
 
-__device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], uint8_t *lds,
-                                                   const uint16_t *__restrict__ bias, void *__restrict__ Y,
-                                                   bool y_f32, int M, int N, int m0, int n0, int wn, int wm,
-                                                   int tid) {
+template <int WN>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[2][2], uint8_t *lds, const uint16_t *__restrict__ bias,
+                                           void *__restrict__ Y, bool y_f32, int M, int N, int m0, int n0, int wn,
+                                           int wm, int tid) {
+    constexpr int BN = 64 * WN;
+    constexpr int THREADS = 128 * WN;
     const int lane = tid & 63, r32 = lane & 31, lh = lane >> 5;
     // row pitches padded by 8 / 16 bytes so that the 32 rows one write
     // instruction touches spread over the banks
-    const int pitch = y_f32 ? 528 : 264;
-    const int cpr = y_f32 ? 32 : 16;  // 16-byte pieces per row of 128 columns
-    const int cols = y_f32 ? 4 : 8;   // columns per piece
+    const int pitch = y_f32 ? 4 * BN + 16 : 2 * BN + 8;
+    const int cpr = y_f32 ? BN / 4 : BN / 8;  // 16-byte pieces per row
+    const int cols = y_f32 ? 4 : 8;           // columns per piece
     for (int p = 0; p < 2; ++p) {
         if (wm == p) {
 #pragma unroll
@@ -122,16 +126,16 @@ __device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], ui
 #pragma unroll
                         for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * qq + t] + bv[t];
                         if (y_f32)
-                            *reinterpret_cast<f32x4 *>(lds + ml * 528 + nl * 4) = f32x4{v[0], v[1], v[2], v[3]};
+                            *reinterpret_cast<f32x4 *>(lds + ml * pitch + nl * 4) = f32x4{v[0], v[1], v[2], v[3]};
                         else
-                            *reinterpret_cast<u32x2 *>(lds + ml * 264 + nl * 2) =
+                            *reinterpret_cast<u32x2 *>(lds + ml * pitch + nl * 2) =
                                 u32x2{bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
                     }
                 }
             }
         }
         __syncthreads();
-        for (int c = tid; c < 64 * cpr; c += 256) {
+        for (int c = tid; c < 64 * cpr; c += THREADS) {
             const int row = c / cpr, piece = c % cpr;
             const int m = m0 + 64 * p + row, n = n0 + piece * cols;
             if (m < M && n < N) {
@@ -144,6 +148,13 @@ __device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], ui
         }
         __syncthreads();
     }
+}
+
+__device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], uint8_t *lds,
+                                                   const uint16_t *__restrict__ bias, void *__restrict__ Y,
+                                                   bool y_f32, int M, int N, int m0, int n0, int wn, int wm,
+                                                   int tid) {
+    store_tile<2>(acc, lds, bias, Y, y_f32, M, N, m0, n0, wn, wm, tid);
 }
 
 }  // namespace svdq

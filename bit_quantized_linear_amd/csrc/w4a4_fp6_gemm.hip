@@ -15,8 +15,12 @@
 // block scales (2^3 on each operand) bring the product back to integers, so
 // one v_mfma_scale_f32_32x32x64_f8f6f4 (K = 64 = one group) returns the
 // group's partial P exactly in fp32 (|P| <= 3136). There is no nibble unpack
-// and no integer-to-float conversion; the vector ALU does one multiply (the
-// scale product) and one FMA per output element and group.
+// and no integer-to-float conversion. The scale products sx[g, m] sw[g, n]
+// come from the matrix core too: an fp32 MFMA with K = 1 is an outer
+// product, and the two-block v_mfma_f32_32x32x1_2b_f32 returns the products
+// of two 32 x 32 tiles in the same lane layout as their partials, each
+// rounded once as a VALU multiply rounds it. The vector ALU does one FMA per
+// output element and group.
 //
 // Block tile 128 (n) x 128 (m), 4 waves as 2 x 2, wave tile 64 x 64 (2 x 2
 // MFMA tiles of 32 x 32). One LDS stage holds two groups (K = 128): per
@@ -62,6 +66,7 @@ constexpr int GB = 48;           // container bytes per row and group
 constexpr int E8M0_X8 = 127 + 3; // MFMA block scale 2^3
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int TILE = 128 * GB;  // one group of a 128-row block: 6 KB
@@ -302,7 +307,7 @@ __device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t 
 }
 
 template <int kEpi>
-__global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
+__global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
     const uint8_t *__restrict__ qx, const float *__restrict__ sx, const uint16_t *__restrict__ T,
     const uint8_t *__restrict__ qw, const float *__restrict__ sw, const uint16_t *__restrict__ l2t,
     const uint16_t *__restrict__ bias, int M, int N, int K, int rank, void *__restrict__ Y, bool y_f32,
@@ -347,24 +352,21 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
         soff[i] = (uint32_t)((side ? n0 : m0) + half * 64 + lane) * 4u;
     }
     // byte offsets of this lane's operand pieces within a staged operand:
-    // [tile][slot][0 = 16-byte piece of plane lh, 1 = 8-byte piece of plane 2]
-    int aoff[2][KG][2], boff[2][KG][2];
+    // row r's 16-byte piece of plane lh at r * 48 + 16 lh, its 8-byte piece
+    // of plane 2 at r * 48 + 32 + 8 lh; tile i (rows + 32 i) and slot q
+    // (+ q TILE) are immediates. The 8-byte pieces of the two row tiles get
+    // bases the compiler cannot see through: otherwise it pairs them into
+    // one ds_read2 and needs moves to place each half next to its 16-byte
+    // piece in the MFMA operand.
+    const int a16 = (wn * 64 + r32) * GB + 16 * lh;
+    const int b16 = (wm * 64 + r32) * GB + 16 * lh;
+    int a8[2], b8[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int ra = wn * 64 + i * 32 + r32;
-        const int rb = wm * 64 + i * 32 + r32;
-#pragma unroll
-        for (int q = 0; q < KG; ++q) {
-            aoff[i][q][0] = q * TILE + ra * GB + 16 * lh;
-            aoff[i][q][1] = q * TILE + ra * GB + 32 + 8 * lh;
-            boff[i][q][0] = q * TILE + rb * GB + 16 * lh;
-            boff[i][q][1] = q * TILE + rb * GB + 32 + 8 * lh;
-            // Opaque to the compiler: otherwise it pairs the 8-byte reads of
-            // two tiles into one ds_read2 and then needs moves to place each
-            // half next to its 16-byte piece in the MFMA operand.
-            asm volatile("" : "+v"(aoff[i][q][1]));
-            asm volatile("" : "+v"(boff[i][q][1]));
-        }
+        a8[i] = (wn * 64 + i * 32 + r32) * GB + 32 + 8 * lh;
+        b8[i] = (wm * 64 + i * 32 + r32) * GB + 32 + 8 * lh;
+        asm volatile("" : "+v"(a8[i]));
+        asm volatile("" : "+v"(b8[i]));
     }
 
     // Every offset is carried whole in the per-lane offset, so a load that
@@ -403,6 +405,7 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const f32x32 zero32 = {};
 
     issue_stage(0, stage[0]);
     __builtin_amdgcn_s_waitcnt(0);
@@ -415,36 +418,40 @@ __global__ __launch_bounds__(THREADS, 2) void w4a4_fp6_kernel(
 #pragma unroll
         for (int q = 0; q < KG; ++q) {
             if (q >= ng) break;
-            i32x8 a[2], b[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                a[i] = frag6(cur.a, aoff[i][q][0], aoff[i][q][1]);
-                b[i] = frag6(cur.b, boff[i][q][0], boff[i][q][1]);
-            }
             if constexpr (kLinear) {
-                // tiles t = (in, im) in order (0,0) (0,1) (1,0) (1,1); the MFMA
-                // of tile t + 1 is issued before the rescale of tile t, so the
-                // rescale never waits for a just-issued MFMA
-                f32x16 P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0], b[0], zero16, 2, 2, 0,
-                                                                           E8M0_X8, 0, E8M0_X8);
+                // per token slice im: one two-block fp32 MFMA (K = 1) gives
+                // the scale products sw[n] sx[m] of tiles (0, im) and (1, im)
+                // in the partials' layout (A = sw of the wave's 64 weight
+                // rows, lane l: row l; B = sx of the slice's 32 tokens, lanes
+                // l and l + 32: token l % 32), rounded once as a VALU multiply
+                // would; the vector ALU is left one FMA per element
+                const i32x8 a0 = frag6(cur.a, q * TILE + a16, q * TILE + a8[0]);
+                const i32x8 a1 = frag6(cur.a, q * TILE + a16 + 32 * GB, q * TILE + a8[1]);
+                const float swv = cur.sa[q][wn * 64 + lane];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int in = t >> 1, im = t & 1;
-                    f32x16 Pn;
-                    if (t + 1 < 4)
-                        Pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[(t + 1) >> 1], b[(t + 1) & 1], zero16,
-                                                                             2, 2, 0, E8M0_X8, 0, E8M0_X8);
-                    const float sxm = cur.sb[q][wm * 64 + im * 32 + r32];
+                for (int im = 0; im < 2; ++im) {
+                    // keep the scheduler from hoisting the next slice's
+                    // operands (and their registers) into this one
+                    __builtin_amdgcn_sched_barrier(0);
+                    const i32x8 bm = frag6(cur.b, q * TILE + b16 + im * 32 * GB, q * TILE + b8[im]);
+                    const float sxv = cur.sb[q][wm * 64 + im * 32 + r32];
+                    const f32x32 C = __builtin_amdgcn_mfma_f32_32x32x1f32(swv, sxv, zero32, 0, 0, 0);
+                    const f32x16 P0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bm, zero16, 2, 2, 0,
+                                                                                      E8M0_X8, 0, E8M0_X8);
+                    const f32x16 P1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bm, zero16, 2, 2, 0,
+                                                                                      E8M0_X8, 0, E8M0_X8);
 #pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) {
-                        const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&cur.sa[q][wn * 64 + in * 32 + 8 * qq + 4 * lh]);
+                    for (int e = 0; e < 16; ++e) acc[0][im][e] = fmaf(C[e], P0[e], acc[0][im][e]);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            acc[in][im][4 * qq + u] = fmaf(sxm * s4[u], P[4 * qq + u], acc[in][im][4 * qq + u]);
-                    }
-                    if (t + 1 < 4) P = Pn;
+                    for (int e = 0; e < 16; ++e) acc[1][im][e] = fmaf(C[16 + e], P1[e], acc[1][im][e]);
                 }
             } else {
+                i32x8 a[2], b[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    a[i] = frag6(cur.a, q * TILE + a16 + i * 32 * GB, q * TILE + a8[i]);
+                    b[i] = frag6(cur.b, q * TILE + b16 + i * 32 * GB, q * TILE + b8[i]);
+                }
 #pragma unroll
                 for (int in = 0; in < 2; ++in) {
 #pragma unroll

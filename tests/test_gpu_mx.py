@@ -149,6 +149,8 @@ def test_mx_quantize_act_tiny_and_zero_blocks():
 @pytest.mark.parametrize("M,K,N,rank,out", [
     (64, 256, 256, 16, "f32"), (64, 256, 256, 16, "bf16"), (77, 320, 40, 32, "bf16"), (1, 64, 8, 0, "f32"),
     (130, 192, 136, 64, "bf16"), (257, 512, 264, 32, "f32"),
+    # large grids with ragged token and weight tails
+    (1300, 256, 12352, 32, "bf16"), (1300, 128, 12416, 16, "f32"),
 ])
 def test_mx_linear_matches_oracle(M, K, N, rank, out):
     say("mx linear", M, K, N, rank, out)
