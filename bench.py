@@ -62,7 +62,7 @@ CSRC = os.path.join(ROOT, "bit_quantized_linear_amd", "csrc")
 GEMM_SOURCES = ("w4a4_fp6_gemm.hip", "device_common.h")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "svdq_w4a4_linear_fp6_mlp_up_4608x3072x12288_traffic.txt")
 COPY_BYTES = 256 << 20  # calibration kernel: reads and writes this many bytes
-GEMM_KERNEL_KEY = "w4a4_fp6_kernel<true>"
+GEMM_KERNEL_KEY = "w4a4_fp6_kernel<0>"
 COPY_KERNEL_KEY = "neg_kernel"
 W16_SOURCES = ("w4a16.hip", "device_common.h")
 W16_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "w4a16_linear_modulation_2x3072x18432_traffic.txt")
