@@ -26,7 +26,8 @@ a HIP graph of launches round-robin over 16 copies of the weight (twice the
 last-level cache), replayed back to back between two HIP events.
 
 HBM traffic of the GEMM comes from two rocprofv3 counter runs (FETCH_SIZE,
-then WRITE_SIZE) of this script with --calibrate-copy, which adds a plain
+then WRITE_SIZE) of this script with --calibrate-copy --no-mlp --no-w8a8 (so
+that each kernel runs at one shape), which adds a plain
 elementwise kernel of known size (a negation, N bytes in, N bytes out) whose
 counter readings give the scale from counter units to bytes:
 
