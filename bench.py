@@ -60,7 +60,7 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
 METRIC = "W4A4+lowrank linear TOPS & % int8 MFMA roofline at M=4608,K=3072,N=12288"
 
 CSRC = os.path.join(ROOT, "bit_quantized_linear_amd", "csrc")
-GEMM_SOURCES = ("w4a4_fp6_gemm.hip", "device_common.h")
+GEMM_SOURCES = ("w4a4_fp6_gemm.hip", "device_common.h", "quant_common.h", "gelu.h")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "svdq_w4a4_linear_fp6_mlp_up_4608x3072x12288_traffic.txt")
 COPY_BYTES = 256 << 20  # calibration kernel: reads and writes this many bytes
 GEMM_KERNEL_KEY = "w4a4_fp6_kernel<0>"

@@ -25,8 +25,17 @@ __global__ __launch_bounds__(256) void tpart_reduce_kernel(const float *__restri
     const size_t n = (size_t)M * rank;
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
+    // loads eight partials ahead of the adds (the adds stay in order)
     float v = 0.0f;
-    for (int c = 0; c < parts; ++c) v += tpart[(size_t)c * n + i];
+    int c = 0;
+    for (; c + 8 <= parts; c += 8) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = tpart[(size_t)(c + j) * n + i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v += p[j];
+    }
+    for (; c < parts; ++c) v += tpart[(size_t)c * n + i];
     T[i] = (uint16_t)f32_to_bf16_bits(v);
 }
 

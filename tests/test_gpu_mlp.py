@@ -161,3 +161,20 @@ def test_fused_mlp_up_full_shape_sampled_rows():
                       abi_d, bd["bits"], 640, N2, N, 32, "bf16", FP6, H.weights_bytes(prep_d, abi_d, FP6))
     ref = sq.forward(side["g"], prep_d, bd["values"], "bf16")
     check_output(H.y_values(Yd, "bf16"), ref["y"])
+
+
+def test_fused_pair_without_bias_and_deterministic():
+    """No up-projection bias; two runs give identical bytes."""
+    M, K, N, N2, rank, rank_down = 150, 192, 384, 64, 16, 32
+    say("mlp pair no bias")
+    p, prep_d, abi_d, _ = pair_problem(M, K, N, N2, rank, rank_down, seed=23)
+    a = run_fused(p["X"]["bits"], p["abi"], p["prep"], None, abi_d, M, N, K, rank, rank_down)
+    c = run_fused(p["X"]["bits"], p["abi"], p["prep"], None, abi_d, M, N, K, rank, rank_down)
+    for key in ("qxd", "sxd", "Td", "yup"):
+        assert np.array_equal(H.host(a[key]), H.host(c[key])), key
+    y_up = sq.bf16_from_bits(H.host(a["yup"]).view(np.uint16))
+    check_output(y_up, sq.forward(p["X"]["values"], p["prep"], None, "bf16")["y"])
+    side = mlp.down_activation_side(y_up, prep_d)
+    assert np.array_equal(H.host(a["qxd"]), pack_fp6(side["qx"]))
+    assert np.array_equal(H.host(a["sxd"]), side["sx"])
+    check_T(a["Td"], side["T"], side["g"], prep_d["L1s"])
