@@ -77,84 +77,108 @@ __device__ __forceinline__ void unpack_int4x16(uint32_t a, uint32_t b, uint32_t 
 }
 
 // ---- Output tile store through LDS -----------------------------------------
-// A block's (64 WN) (n) x 128 (m) output tile, held by WN x 2 waves (wn, wm)
-// as 2 x 2 32x32 fp32 MFMA tiles each (lane: column m = wm 64 + im 32 +
-// l % 32, rows n = wn 64 + in 32 + 8 qq + 4 (l / 32) + t), plus bias[n],
-// rounded to bf16 (nearest even) or kept fp32, stored to Y [M][N] (row m, N
-// contiguous). Stored straight from the MFMA layout, one instruction would
-// write 16 bytes into each of 32 rows; staged through LDS instead, in two
-// passes of 64 tokens (the waves of one wm row write, everyone stores), each
-// 16-byte piece of a row segment of 128 WN (bf16) or 256 WN (fp32) bytes is
-// stored by one lane, consecutive lanes along the row.
+// A block's 128 (n) x 128 (m) output tile, held by 2 x 2 waves (wn, wm) as
+// 2 x 2 32x32 fp32 MFMA tiles each (lane: column m = wm 64 + im 32 + l % 32,
+// rows n = wn 64 + in 32 + 8 qq + 4 (l / 32) + t), plus bias[n], rounded to
+// bf16 (nearest even) or kept fp32, stored to Y [M][N] (row m, N contiguous).
+// Stored straight from the MFMA layout, one instruction would write 16 bytes
+// into each of 32 rows; staged through LDS instead, each 16-byte piece of a
+// row segment (256 bytes bf16, 512 bytes fp32) is stored by one lane,
+// consecutive lanes along the row. A bf16 tile goes through LDS whole (every
+// wave writes at once, one barrier); an fp32 tile in two passes of 64 tokens
+// (the waves of one wm row write, everyone stores). Row pitches are padded
+// by 8 / 16 bytes so that the 32 rows one write instruction touches spread
+// over the banks.
+// The bias comes from LDS as fp32 (stage_bias_128 at the start of the
+// kernel, so no global load waits after the main loop).
 // Needs N % 8 == 0 and Y 16-byte aligned (16-byte pieces never straddle the
-// end of a row), `lds` >= tile_store_lds_bytes(WN) bytes not in use by
-// anyone, and all 128 WN threads of the block (it synchronizes).
-constexpr int tile_store_lds_bytes(int WN) { return 64 * (256 * WN + 16); }
-constexpr int kTileStoreLdsBytes = tile_store_lds_bytes(2);
+// end of a row), `lds` >= kTileStoreLdsBytes bytes not in use by anyone, and
+// all 256 threads of the block (it synchronizes).
+constexpr int kTileBf16Pitch = 2 * 128 + 8;
+constexpr int kTileF32Pitch = 4 * 128 + 16;
+constexpr int kTileStoreLdsBytes = 128 * kTileBf16Pitch > 64 * kTileF32Pitch ? 128 * kTileBf16Pitch
+                                                                              : 64 * kTileF32Pitch;
 
-template <int WN>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[2][2], uint8_t *lds, const uint16_t *__restrict__ bias,
-                                           void *__restrict__ Y, bool y_f32, int M, int N, int m0, int n0, int wn,
-                                           int wm, int tid) {
-    constexpr int BN = 64 * WN;
-    constexpr int THREADS = 128 * WN;
+// The block's 128 bias values bias[n0 .. n0 + 127] as fp32 into bias_s (16-
+// byte aligned LDS), zero past N or without bias. A barrier between this and
+// the first read makes them visible; the GEMM kernels call it before the
+// barrier that precedes their main loop.
+__device__ __forceinline__ void stage_bias_128(float *bias_s, const uint16_t *__restrict__ bias, int n0, int N,
+                                               int tid) {
+    if (tid < 128) bias_s[tid] = bias && n0 + tid < N ? bf16_bits_to_f32(bias[n0 + tid]) : 0.0f;
+}
+
+__device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], uint8_t *lds, const float *bias_s,
+                                                   void *__restrict__ Y, bool y_f32, int M, int N, int m0, int n0,
+                                                   int wn, int wm, int tid) {
     const int lane = tid & 63, r32 = lane & 31, lh = lane >> 5;
-    // row pitches padded by 8 / 16 bytes so that the 32 rows one write
-    // instruction touches spread over the banks
-    const int pitch = y_f32 ? 4 * BN + 16 : 2 * BN + 8;
-    const int cpr = y_f32 ? BN / 4 : BN / 8;  // 16-byte pieces per row
-    const int cols = y_f32 ? 4 : 8;           // columns per piece
+    if (!y_f32) {
+#pragma unroll
+        for (int in = 0; in < 2; ++in) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int nl = wn * 64 + in * 32 + 8 * qq + 4 * lh;
+                const f32x4 bv = *reinterpret_cast<const f32x4 *>(bias_s + nl);
+#pragma unroll
+                for (int im = 0; im < 2; ++im) {
+                    const int ml = wm * 64 + im * 32 + r32;
+                    float v[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * qq + t] + bv[t];
+                    *reinterpret_cast<u32x2 *>(lds + ml * kTileBf16Pitch + nl * 2) =
+                        u32x2{bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
+                }
+            }
+        }
+        __syncthreads();
+        uint16_t *y = static_cast<uint16_t *>(Y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = tid + 256 * i;  // 128 rows x 16 pieces
+            const int row = c >> 4, piece = c & 15;
+            const int m = m0 + row, n = n0 + piece * 8;
+            if (m < M && n < N) {
+                // rows are 8-byte aligned (264-byte pitch): two 8-byte reads
+                const uint8_t *src = lds + row * kTileBf16Pitch + piece * 16;
+                const u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
+                const u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 8);
+                *reinterpret_cast<u32x4 *>(y + (size_t)m * N + n) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+        }
+        return;
+    }
+    float *y = static_cast<float *>(Y);
     for (int p = 0; p < 2; ++p) {
+        if (p) __syncthreads();  // the first pass's reads are done
         if (wm == p) {
 #pragma unroll
             for (int in = 0; in < 2; ++in) {
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) {
                     const int nl = wn * 64 + in * 32 + 8 * qq + 4 * lh;
-                    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (bias && n0 + nl < N) {
-                        const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n0 + nl);
-                        bv[0] = bf16_bits_to_f32(bb[0] & 0xFFFFu);
-                        bv[1] = bf16_bits_to_f32(bb[0] >> 16);
-                        bv[2] = bf16_bits_to_f32(bb[1] & 0xFFFFu);
-                        bv[3] = bf16_bits_to_f32(bb[1] >> 16);
-                    }
+                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(bias_s + nl);
 #pragma unroll
                     for (int im = 0; im < 2; ++im) {
                         const int ml = im * 32 + r32;
-                        float v[4];
+                        f32x4 v;
 #pragma unroll
                         for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * qq + t] + bv[t];
-                        if (y_f32)
-                            *reinterpret_cast<f32x4 *>(lds + ml * pitch + nl * 4) = f32x4{v[0], v[1], v[2], v[3]};
-                        else
-                            *reinterpret_cast<u32x2 *>(lds + ml * pitch + nl * 2) =
-                                u32x2{bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
+                        *reinterpret_cast<f32x4 *>(lds + ml * kTileF32Pitch + nl * 4) = v;
                     }
                 }
             }
         }
         __syncthreads();
-        for (int c = tid; c < 64 * cpr; c += THREADS) {
-            const int row = c / cpr, piece = c % cpr;
-            const int m = m0 + 64 * p + row, n = n0 + piece * cols;
-            if (m < M && n < N) {
-                const uint8_t *src = lds + row * pitch + piece * 16;
-                const u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
-                const u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 8);
-                uint8_t *dst = static_cast<uint8_t *>(Y) + ((size_t)m * N + n) * (y_f32 ? 4 : 2);
-                *reinterpret_cast<u32x4 *>(dst) = u32x4{lo[0], lo[1], hi[0], hi[1]};
-            }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = tid + 256 * i;  // 64 rows x 32 pieces
+            const int row = c >> 5, piece = c & 31;
+            const int m = m0 + 64 * p + row, n = n0 + piece * 4;
+            if (m < M && n < N)
+                *reinterpret_cast<u32x4 *>(y + (size_t)m * N + n) =
+                    *reinterpret_cast<const u32x4 *>(lds + row * kTileF32Pitch + piece * 16);
         }
-        __syncthreads();
     }
-}
-
-__device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], uint8_t *lds,
-                                                   const uint16_t *__restrict__ bias, void *__restrict__ Y,
-                                                   bool y_f32, int M, int N, int m0, int n0, int wn, int wm,
-                                                   int tid) {
-    store_tile<2>(acc, lds, bias, Y, y_f32, M, N, m0, n0, wn, wm, tid);
 }
 
 }  // namespace svdq

@@ -72,7 +72,8 @@ __global__ __launch_bounds__(MX_THREADS, 3) void mx_linear_kernel(
     const uint8_t *__restrict__ qw, const uint8_t *__restrict__ uw, const uint16_t *__restrict__ l2t,
     const uint16_t *__restrict__ bias, int M, int N, int K, int ldm, int ldn, int rank,
     void *__restrict__ Y, bool y_f32, int tiles_n) {
-    __shared__ StageMx stage[MX_NS];
+    __shared__ __attribute__((aligned(16))) StageMx stage[MX_NS];
+    __shared__ __attribute__((aligned(16))) float bias_s[128];
 
     const int tile_n = blockIdx.x % tiles_n;
     const int tile_m = blockIdx.x / tiles_n;
@@ -152,6 +153,7 @@ __global__ __launch_bounds__(MX_THREADS, 3) void mx_linear_kernel(
             __builtin_amdgcn_s_waitcnt(0);
     };
 
+    stage_bias_128(bias_s, bias, n0, N, tid);
     issue_stage(0, stage[0]);
     if (S > 1) issue_stage(1, stage[1]);
     wait_loads(loads_of(1));
@@ -212,7 +214,8 @@ __global__ __launch_bounds__(MX_THREADS, 3) void mx_linear_kernel(
     // every load has landed and been read: the stage buffers hold the
     // output tile on its way out
     static_assert(sizeof(StageMx) * MX_NS >= kTileStoreLdsBytes, "LDS too small for the output tile");
-    store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias, Y, y_f32, M, N, m0, n0, wn, wm, tid);
+    store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias_s, Y, y_f32, M, N, m0, n0, wn, wm,
+                       tid);
 }
 
 }  // namespace

@@ -117,8 +117,8 @@ constexpr int kMlpLdsBytes = kMlpTabOff + kGeluTableEntries * 2;
 // tile's 128 rows of L1s (16x16x32 bf16 MFMAs, fp32 accumulation) and
 // stores the fp32 partial of T for this column tile. Columns past N (N is
 // a multiple of 64, so a whole group) give g = 0 and are not written.
-__device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t *lds,
-                                             const uint16_t *__restrict__ bias, const MlpOut &o, int M, int N,
+__device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t *lds, const float *bias_s,
+                                             const MlpOut &o, int M, int N,
                                              int m0, int n0, int tile_n, int wn, int wm, int tid) {
     const int lane = tid & 63, r32 = lane & 31, lh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -144,14 +144,7 @@ __device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t 
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) {
                     const int nl = wn * 64 + in * 32 + 8 * qq + 4 * lh;
-                    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (bias && n0 + nl < N) {
-                        const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n0 + nl);
-                        bv[0] = bf16_bits_to_f32(bb[0] & 0xFFFFu);
-                        bv[1] = bf16_bits_to_f32(bb[0] >> 16);
-                        bv[2] = bf16_bits_to_f32(bb[1] & 0xFFFFu);
-                        bv[3] = bf16_bits_to_f32(bb[1] >> 16);
-                    }
+                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(bias_s + nl);
 #pragma unroll
                     for (int im = 0; im < 2; ++im) {
                         const int ml = im * 32 + r32;
@@ -407,6 +400,8 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
     const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const f32x32 zero32 = {};
 
+    __shared__ __attribute__((aligned(16))) float bias_s[BN];
+    if constexpr (kLinear) stage_bias_128(bias_s, bias, n0, N, tid);
     issue_stage(0, stage[0]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -506,9 +501,10 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
         static_assert(sizeof(Stage6) * 2 >= kTileStoreLdsBytes, "LDS too small for the output tile");
         static_assert(sizeof(Stage6) * 2 >= kMlpLdsBytes, "LDS too small for the MLP epilogue");
         if constexpr (kEpi == kEpiMlp)
-            mlp_epilogue(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias, mlp, M, N, m0, n0, tile_n, wn, wm, tid);
+            mlp_epilogue(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias_s, mlp, M, N, m0, n0, tile_n, wn, wm,
+                         tid);
         else
-            store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias, Y, y_f32, M, N, m0, n0, wn, wm,
+            store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias_s, Y, y_f32, M, N, m0, n0, wn, wm,
                                tid);
     }
 }

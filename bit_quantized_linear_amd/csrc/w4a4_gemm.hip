@@ -32,7 +32,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void w4a4_gemm_kernel(
     const uint8_t *__restrict__ qw, const float *__restrict__ sw, const uint16_t *__restrict__ l2t,
     const uint16_t *__restrict__ bias, int M, int N, int K, int rank, void *__restrict__ Y,
     bool y_f32, int32_t *__restrict__ Pout, int tiles_n) {
-    __shared__ GemmStage stage[2];
+    __shared__ __attribute__((aligned(16))) GemmStage stage[2];
+    __shared__ __attribute__((aligned(16))) float bias_s[kTileN];
 
     const int tile_n = blockIdx.x % tiles_n;
     const int tile_m = blockIdx.x / tiles_n;
@@ -57,6 +58,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void w4a4_gemm_kernel(
     StepRegs<true> regs;
     load_step<true, kEpi == W4Epilogue::kLinear>(regs, qw, qx, sw, sx, n0, m0, N, M, K, 0);
     store_step<true>(stage[0], regs);
+    if constexpr (kEpi == W4Epilogue::kLinear) stage_bias_128(bias_s, bias, n0, N, threadIdx.x);
     __syncthreads();
 
     for (int g = 0; g < G; ++g) {
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void w4a4_gemm_kernel(
         // every stage has been read: the stage buffers hold the output tile on
         // its way out
         static_assert(sizeof(GemmStage) * 2 >= kTileStoreLdsBytes, "LDS too small for the output tile");
-        store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias, Y, y_f32, M, N, m0, n0, wn, wm,
+        store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias_s, Y, y_f32, M, N, m0, n0, wn, wm,
                            threadIdx.x);
     }
 }

@@ -126,7 +126,8 @@ __global__ __launch_bounds__(W8_THREADS, 2) void w8a8_gemm_kernel(
     const int8_t *__restrict__ qx, const int8_t *__restrict__ qw, const float *__restrict__ sxp,
     float sw, const uint16_t *__restrict__ bias, int M, int N, int K, uint16_t *__restrict__ Y,
     int32_t *__restrict__ acc_out, int tiles_n) {
-    __shared__ W8Stage stage[2];
+    __shared__ __attribute__((aligned(16))) W8Stage stage[2];
+    __shared__ __attribute__((aligned(16))) float bias_s[W8_TILE];
 
     const int tile_n = blockIdx.x % tiles_n;
     const int tile_m = blockIdx.x / tiles_n;
@@ -190,6 +191,7 @@ __global__ __launch_bounds__(W8_THREADS, 2) void w8a8_gemm_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) P[i][j][e] = 0;
 
+    if constexpr (kEpi == W8Epilogue::kLinear) stage_bias_128(bias_s, bias, n0, N, threadIdx.x);
     issue_stage(0, stage[0]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(W8_THREADS, 2) void w8a8_gemm_kernel(
         // every stage has been read: the stage buffers hold the output tile
         // on its way out
         static_assert(sizeof(W8Stage) * 2 >= kTileStoreLdsBytes, "LDS too small for the output tile");
-        store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias, Y, false, M, N, m0, n0, wn, wm,
+        store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias_s, Y, false, M, N, m0, n0, wn, wm,
                            threadIdx.x);
     } else {
 #pragma unroll
