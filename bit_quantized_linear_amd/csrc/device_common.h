@@ -91,13 +91,19 @@ __device__ __forceinline__ void unpack_int4x16(uint32_t a, uint32_t b, uint32_t 
 // over the banks.
 // The bias comes from LDS as fp32 (stage_bias_128 at the start of the
 // kernel, so no global load waits after the main loop).
+// The LDS tile is held in two halves, lds_lo for the first half of the rows
+// in LDS at a time and lds_hi for the second (two stage buffers of the
+// caller, which need not be adjacent: kernels keep their stages in separate
+// LDS variables so that the compiler can tell a stage being refilled from
+// the one being read).
 // Needs N % 8 == 0 and Y 16-byte aligned (16-byte pieces never straddle the
-// end of a row), `lds` >= kTileStoreLdsBytes bytes not in use by anyone, and
-// all 256 threads of the block (it synchronizes).
+// end of a row), lds_lo and lds_hi >= kTileHalfLdsBytes bytes each, 16-byte
+// aligned and not in use by anyone, and all 256 threads of the block (it
+// synchronizes).
 constexpr int kTileBf16Pitch = 2 * 128 + 8;
 constexpr int kTileF32Pitch = 4 * 128 + 16;
-constexpr int kTileStoreLdsBytes = 128 * kTileBf16Pitch > 64 * kTileF32Pitch ? 128 * kTileBf16Pitch
-                                                                              : 64 * kTileF32Pitch;
+constexpr int kTileHalfLdsBytes = 64 * kTileBf16Pitch > 32 * kTileF32Pitch ? 64 * kTileBf16Pitch
+                                                                             : 32 * kTileF32Pitch;
 
 // The block's 128 bias values bias[n0 .. n0 + 127] as fp32 into bias_s (16-
 // byte aligned LDS), zero past N or without bias. A barrier between this and
@@ -108,9 +114,9 @@ __device__ __forceinline__ void stage_bias_128(float *bias_s, const uint16_t *__
     if (tid < 128) bias_s[tid] = bias && n0 + tid < N ? bf16_bits_to_f32(bias[n0 + tid]) : 0.0f;
 }
 
-__device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], uint8_t *lds, const float *bias_s,
-                                                   void *__restrict__ Y, bool y_f32, int M, int N, int m0, int n0,
-                                                   int wn, int wm, int tid) {
+__device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], uint8_t *lds_lo, uint8_t *lds_hi,
+                                                   const float *bias_s, void *__restrict__ Y, bool y_f32, int M,
+                                                   int N, int m0, int n0, int wn, int wm, int tid) {
     const int lane = tid & 63, r32 = lane & 31, lh = lane >> 5;
     if (!y_f32) {
 #pragma unroll
@@ -121,11 +127,12 @@ __device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], ui
                 const f32x4 bv = *reinterpret_cast<const f32x4 *>(bias_s + nl);
 #pragma unroll
                 for (int im = 0; im < 2; ++im) {
-                    const int ml = wm * 64 + im * 32 + r32;
+                    // rows 0..63 (wm = 0) in the low half, 64..127 in the high
+                    const int ml = im * 32 + r32;
                     float v[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * qq + t] + bv[t];
-                    *reinterpret_cast<u32x2 *>(lds + ml * kTileBf16Pitch + nl * 2) =
+                    *reinterpret_cast<u32x2 *>((wm ? lds_hi : lds_lo) + ml * kTileBf16Pitch + nl * 2) =
                         u32x2{bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
                 }
             }
@@ -139,7 +146,8 @@ __device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], ui
             const int m = m0 + row, n = n0 + piece * 8;
             if (m < M && n < N) {
                 // rows are 8-byte aligned (264-byte pitch): two 8-byte reads
-                const uint8_t *src = lds + row * kTileBf16Pitch + piece * 16;
+                const uint8_t *src = (row < 64 ? lds_lo + row * kTileBf16Pitch
+                                               : lds_hi + (row - 64) * kTileBf16Pitch) + piece * 16;
                 const u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
                 const u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 8);
                 *reinterpret_cast<u32x4 *>(y + (size_t)m * N + n) = u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -159,11 +167,11 @@ __device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], ui
                     const f32x4 bv = *reinterpret_cast<const f32x4 *>(bias_s + nl);
 #pragma unroll
                     for (int im = 0; im < 2; ++im) {
-                        const int ml = im * 32 + r32;
+                        // pass rows 0..31 (im = 0) in the low half, 32..63 in the high
                         f32x4 v;
 #pragma unroll
                         for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * qq + t] + bv[t];
-                        *reinterpret_cast<f32x4 *>(lds + ml * kTileF32Pitch + nl * 4) = v;
+                        *reinterpret_cast<f32x4 *>((im ? lds_hi : lds_lo) + r32 * kTileF32Pitch + nl * 4) = v;
                     }
                 }
             }
@@ -175,8 +183,8 @@ __device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], ui
             const int row = c >> 5, piece = c & 31;
             const int m = m0 + 64 * p + row, n = n0 + piece * 4;
             if (m < M && n < N)
-                *reinterpret_cast<u32x4 *>(y + (size_t)m * N + n) =
-                    *reinterpret_cast<const u32x4 *>(lds + row * kTileF32Pitch + piece * 16);
+                *reinterpret_cast<u32x4 *>(y + (size_t)m * N + n) = *reinterpret_cast<const u32x4 *>(
+                    (row < 32 ? lds_lo + row * kTileF32Pitch : lds_hi + (row - 32) * kTileF32Pitch) + piece * 16);
         }
     }
 }

@@ -72,7 +72,12 @@ __global__ __launch_bounds__(MX_THREADS, 3) void mx_linear_kernel(
     const uint8_t *__restrict__ qw, const uint8_t *__restrict__ uw, const uint16_t *__restrict__ l2t,
     const uint16_t *__restrict__ bias, int M, int N, int K, int ldm, int ldn, int rank,
     void *__restrict__ Y, bool y_f32, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) StageMx stage[MX_NS];
+    // the stages in separate LDS variables: the compiler can then tell a
+    // stage being refilled (direct-to-LDS loads) from the one being read and
+    // does not make the reads wait for the loads
+    __shared__ __attribute__((aligned(16))) StageMx sm0;
+    __shared__ __attribute__((aligned(16))) StageMx sm1;
+    __shared__ __attribute__((aligned(16))) StageMx sm2;
     __shared__ __attribute__((aligned(16))) float bias_s[128];
 
     const int tile_n = blockIdx.x % tiles_n;
@@ -154,14 +159,14 @@ __global__ __launch_bounds__(MX_THREADS, 3) void mx_linear_kernel(
     };
 
     stage_bias_128(bias_s, bias, n0, N, tid);
-    issue_stage(0, stage[0]);
-    if (S > 1) issue_stage(1, stage[1]);
+    issue_stage(0, sm0);
+    if (S > 1) issue_stage(1, sm1);
     wait_loads(loads_of(1));
     __syncthreads();
 
-    for (int s = 0; s < S; ++s) {
-        const StageMx &cur = stage[s % MX_NS];
-        if (s + 2 < S) issue_stage(s + 2, stage[(s + 2) % MX_NS]);
+    // stage s is read from `cur` while stage s + 2 loads into `refill`
+    auto run_stage = [&](int s, const StageMx &cur, StageMx &refill) {
+        if (s + 2 < S) issue_stage(s + 2, refill);
         const int ng = min(MX_KG, G - s * MX_KG);
         mx_i32x8 a[MX_KG][2], b[MX_KG][2];
         int sa[MX_KG][2], sb[MX_KG][2];
@@ -191,6 +196,12 @@ __global__ __launch_bounds__(MX_THREADS, 3) void mx_linear_kernel(
         // it is refilled (with stage s + 3, issued after the barrier)
         wait_loads(loads_of(s + 2));
         __syncthreads();
+    };
+    // stage s lives in sm(s % 3)
+    for (int s = 0; s < S; s += MX_NS) {
+        run_stage(s, sm0, sm2);
+        if (s + 1 < S) run_stage(s + 1, sm1, sm0);
+        if (s + 2 < S) run_stage(s + 2, sm2, sm1);
     }
 
     // low-rank up-projection T L2 (bf16 MFMA, fp32 accumulation) and bias
@@ -213,9 +224,9 @@ __global__ __launch_bounds__(MX_THREADS, 3) void mx_linear_kernel(
     }
     // every load has landed and been read: the stage buffers hold the
     // output tile on its way out
-    static_assert(sizeof(StageMx) * MX_NS >= kTileStoreLdsBytes, "LDS too small for the output tile");
-    store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias_s, Y, y_f32, M, N, m0, n0, wn, wm,
-                       tid);
+    static_assert(sizeof(StageMx) >= kTileHalfLdsBytes, "LDS too small for the output tile");
+    store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&sm0), reinterpret_cast<uint8_t *>(&sm1), bias_s, Y, y_f32, M,
+                       N, m0, n0, wn, wm, tid);
 }
 
 }  // namespace

@@ -306,7 +306,11 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
     const uint16_t *__restrict__ bias, int M, int N, int K, int rank, void *__restrict__ Y, bool y_f32,
     int32_t *__restrict__ Pout, int tiles_n, MlpOut mlp) {
     constexpr bool kLinear = kEpi != kEpiPartials;
-    __shared__ __attribute__((aligned(16))) Stage6 stage[2];
+    // two stages in separate LDS variables: the compiler can then tell the
+    // stage being refilled (direct-to-LDS loads) from the one being read and
+    // does not make the reads wait for the loads
+    __shared__ __attribute__((aligned(16))) Stage6 st0;
+    __shared__ __attribute__((aligned(16))) Stage6 st1;
 
     const int tile_n = blockIdx.x % tiles_n;
     const int tile_m = blockIdx.x / tiles_n;
@@ -402,13 +406,13 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
 
     __shared__ __attribute__((aligned(16))) float bias_s[BN];
     if constexpr (kLinear) stage_bias_128(bias_s, bias, n0, N, tid);
-    issue_stage(0, stage[0]);
+    issue_stage(0, st0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int s = 0; s < S; ++s) {
-        const Stage6 &cur = stage[s & 1];
-        if (s + 1 < S) issue_stage(s + 1, stage[(s + 1) & 1]);
+    // stage s is read from `cur` while stage s + 1 loads into `nxt`
+    auto run_stage = [&](int s, const Stage6 &cur, Stage6 &nxt) {
+        if (s + 1 < S) issue_stage(s + 1, nxt);
         const int ng = min(KG, G - s * KG);
 #pragma unroll
         for (int q = 0; q < KG; ++q) {
@@ -476,6 +480,10 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
         // refilled
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    for (int s = 0; s < S; s += 2) {
+        run_stage(s, st0, st1);
+        if (s + 1 < S) run_stage(s + 1, st1, st0);
     }
 
     if constexpr (kLinear) {
@@ -498,14 +506,13 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
         }
         // every load has landed and been read: the stage buffers hold the
         // output tile on its way out
-        static_assert(sizeof(Stage6) * 2 >= kTileStoreLdsBytes, "LDS too small for the output tile");
-        static_assert(sizeof(Stage6) * 2 >= kMlpLdsBytes, "LDS too small for the MLP epilogue");
+        static_assert(sizeof(Stage6) >= kTileHalfLdsBytes, "LDS too small for the output tile");
+        static_assert(sizeof(Stage6) >= kMlpLdsBytes, "LDS too small for the MLP epilogue");
         if constexpr (kEpi == kEpiMlp)
-            mlp_epilogue(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias_s, mlp, M, N, m0, n0, tile_n, wn, wm,
-                         tid);
+            mlp_epilogue(acc, reinterpret_cast<uint8_t *>(&st0), bias_s, mlp, M, N, m0, n0, tile_n, wn, wm, tid);
         else
-            store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias_s, Y, y_f32, M, N, m0, n0, wn, wm,
-                               tid);
+            store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&st0), reinterpret_cast<uint8_t *>(&st1), bias_s, Y,
+                               y_f32, M, N, m0, n0, wn, wm, tid);
     }
 }
 

@@ -141,9 +141,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void w4a4_gemm_kernel(
         }
         // every stage has been read: the stage buffers hold the output tile on
         // its way out
-        static_assert(sizeof(GemmStage) * 2 >= kTileStoreLdsBytes, "LDS too small for the output tile");
-        store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias_s, Y, y_f32, M, N, m0, n0, wn, wm,
-                           threadIdx.x);
+        static_assert(sizeof(GemmStage) >= kTileHalfLdsBytes, "LDS too small for the output tile");
+        store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), reinterpret_cast<uint8_t *>(&stage[1]),
+                           bias_s, Y, y_f32, M, N, m0, n0, wn, wm, threadIdx.x);
     }
 }
 

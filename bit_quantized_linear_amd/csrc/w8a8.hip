@@ -126,7 +126,11 @@ __global__ __launch_bounds__(W8_THREADS, 2) void w8a8_gemm_kernel(
     const int8_t *__restrict__ qx, const int8_t *__restrict__ qw, const float *__restrict__ sxp,
     float sw, const uint16_t *__restrict__ bias, int M, int N, int K, uint16_t *__restrict__ Y,
     int32_t *__restrict__ acc_out, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) W8Stage stage[2];
+    // two stages in separate LDS variables: the compiler can then tell the
+    // stage being refilled (direct-to-LDS loads) from the one being read and
+    // does not make the reads wait for the loads
+    __shared__ __attribute__((aligned(16))) W8Stage st0;
+    __shared__ __attribute__((aligned(16))) W8Stage st1;
     __shared__ __attribute__((aligned(16))) float bias_s[W8_TILE];
 
     const int tile_n = blockIdx.x % tiles_n;
@@ -192,12 +196,12 @@ __global__ __launch_bounds__(W8_THREADS, 2) void w8a8_gemm_kernel(
             for (int e = 0; e < 16; ++e) P[i][j][e] = 0;
 
     if constexpr (kEpi == W8Epilogue::kLinear) stage_bias_128(bias_s, bias, n0, N, threadIdx.x);
-    issue_stage(0, stage[0]);
+    issue_stage(0, st0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int s = 0; s < S; ++s) {
-        const W8Stage &cur = stage[s & 1];
-        if (s + 1 < S) issue_stage(s + 1, stage[(s + 1) & 1]);
+    // stage s is read from `cur` while stage s + 1 loads into `nxt`
+    auto run_stage = [&](int s, const W8Stage &cur, W8Stage &nxt) {
+        if (s + 1 < S) issue_stage(s + 1, nxt);
 #pragma unroll
         for (int kk = 0; kk < W8_KS / 32; ++kk) {
             i32x4 a[2], b[2];
@@ -217,6 +221,10 @@ __global__ __launch_bounds__(W8_THREADS, 2) void w8a8_gemm_kernel(
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    for (int s = 0; s < S; s += 2) {
+        run_stage(s, st0, st1);
+        if (s + 1 < S) run_stage(s + 1, st1, st0);
     }
 
     if constexpr (kEpi == W8Epilogue::kLinear) {
@@ -231,9 +239,9 @@ __global__ __launch_bounds__(W8_THREADS, 2) void w8a8_gemm_kernel(
                 for (int e = 0; e < 16; ++e) acc[in][im][e] = (float)P[in][im][e] * scale;
         // every stage has been read: the stage buffers hold the output tile
         // on its way out
-        static_assert(sizeof(W8Stage) * 2 >= kTileStoreLdsBytes, "LDS too small for the output tile");
-        store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&stage[0]), bias_s, Y, false, M, N, m0, n0, wn, wm,
-                           threadIdx.x);
+        static_assert(sizeof(W8Stage) >= kTileHalfLdsBytes, "LDS too small for the output tile");
+        store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&st0), reinterpret_cast<uint8_t *>(&st1), bias_s, Y,
+                           false, M, N, m0, n0, wn, wm, threadIdx.x);
     } else {
 #pragma unroll
         for (int in = 0; in < 2; ++in) {
