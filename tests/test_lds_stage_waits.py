@@ -1,0 +1,82 @@
+"""The GEMMs that stage operands with direct-to-LDS loads keep each stage in
+its own LDS variable so that the compiler can tell the stage being refilled
+from the one being read. With the stages in one array, in a kernel with
+more than one LDS variable, it put a wait for every outstanding load
+(`s_waitcnt vmcnt(0)`) between a stage's refill loads and its first LDS
+read, so each stage waited for loads it had just issued. This compiles the three kernels to gfx950 assembly (host only, no
+GPU) and checks that no such wait sits between a direct-to-LDS load and the
+next LDS read unless a barrier separates them (the intended waits come
+right before the barrier that ends a stage, or the one after the prologue).
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from bit_quantized_linear_amd import build as B
+
+SOURCES = ["w4a4_fp6_gemm.hip", "mx_gemm.hip", "w8a8.hip"]
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.HIPCC) or shutil.which("python3") is None,
+                                reason="hipcc not available")
+
+
+def _assembly(src, tmp_path):
+    os.makedirs(B.BUILD, exist_ok=True)
+    from bit_quantized_linear_amd import gelu_table
+    header = os.path.join(B.BUILD, "gelu_table.h")
+    if not os.path.exists(header):
+        gelu_table.write(header)
+    out = tmp_path / (src + ".s")
+    subprocess.run([B.HIPCC] + B.HIP_FLAGS + ["-I", B.CSRC, "-I", B.BUILD, "--cuda-device-only", "-S",
+                    os.path.join(B.CSRC, src), "-o", str(out)], check=True, capture_output=True)
+    return out.read_text().splitlines()
+
+
+def _stalls(lines):
+    """(line, text) of every vmcnt(0) wait found after a direct-to-LDS load
+    and before the next LDS read, with no barrier and no load into registers
+    in between (text order)."""
+    found = []
+    pending_lds_load = False
+    wait_line = None
+    for i, raw in enumerate(lines):
+        line = raw.strip()
+        if line.endswith(":") or line.startswith(".") and not line.startswith(".LBB"):
+            continue
+        if re.match(r"(buffer|global)_load\S*\s.*\blds\b", line):
+            pending_lds_load, wait_line = True, None
+        elif re.match(r"(buffer|global|flat)_load", line) or line.startswith("s_barrier") or \
+                line.startswith("s_endpgm"):
+            # a load into registers: a later wait may be for it (the epilogue's
+            # low-rank operands); a barrier ends the stage
+            pending_lds_load, wait_line = False, None
+        elif pending_lds_load and line.startswith("s_waitcnt") and re.search(r"vmcnt\(0\)", line):
+            wait_line = (i + 1, line)
+        elif line.startswith("ds_read") and wait_line is not None:
+            found.append(wait_line)
+            pending_lds_load, wait_line = False, None
+    return found
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_reads_do_not_wait_for_the_refill_loads(src, tmp_path):
+    lines = _assembly(src, tmp_path)
+    assert any(re.match(r"\s*buffer_load\S*\s.*\blds\b", l) for l in lines), "no direct-to-LDS loads found"
+    stalls = _stalls(lines)
+    assert not stalls, f"{src}: LDS reads wait for in-flight refill loads at {stalls[:3]}"
+
+
+def test_checker_flags_the_stalling_pattern():
+    """The pattern the one-array stages produced, and the intended forms."""
+    bad = ["buffer_load_dwordx4 v2, s[4:7], 0 offen lds", "s_waitcnt vmcnt(0)", "ds_read_b128 v[8:11], v3"]
+    good_end = ["buffer_load_dwordx4 v2, s[4:7], 0 offen lds", "ds_read_b128 v[8:11], v3",
+                "s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)", "s_barrier", "ds_read_b128 v[8:11], v3"]
+    epilogue = ["buffer_load_dwordx4 v2, s[4:7], 0 offen lds", "global_load_dwordx4 v[4:7], v[0:1], off",
+                "s_waitcnt vmcnt(0)", "ds_read_b128 v[8:11], v3"]
+    assert _stalls(bad) == [(2, "s_waitcnt vmcnt(0)")]
+    assert _stalls(good_end) == []
+    assert _stalls(epilogue) == []
