@@ -105,17 +105,41 @@ def _np_ptr(a, dtype):
     return a.ctypes.data
 
 
-def _dev_ptr(t, itemsize=None):
-    """Device pointer of a torch tensor (None -> NULL)."""
+def _current_device():
+    import torch
+
+    return torch.cuda.current_device()
+
+
+def _dev_ptr(t, itemsize=None, nbytes=0, name="tensor", device=None):
+    """Device pointer of a torch tensor (None -> NULL).
+
+    The library receives raw pointers and sizes, so the extent a call will
+    touch is checked here, before anything is launched: the tensor must be a
+    contiguous GPU tensor on the current device (`device`, looked up when not
+    given) holding at least `nbytes` bytes. A violation raises TypeError
+    (kind, layout, element size, device) or ValueError (too small)."""
     if t is None:
         return None
     if not t.is_cuda:
-        raise TypeError("device entry points take GPU tensors")
+        raise TypeError(f"{name}: device entry points take GPU tensors")
     if not t.is_contiguous():
-        raise TypeError("tensors must be contiguous")
+        raise TypeError(f"{name}: tensors must be contiguous")
     if itemsize is not None and t.element_size() != itemsize:
-        raise TypeError(f"expected {itemsize}-byte elements, got {t.element_size()}")
+        raise TypeError(f"{name}: expected {itemsize}-byte elements, got {t.element_size()}")
+    dev = _current_device() if device is None else device
+    if t.device.index != dev:
+        raise TypeError(f"{name} is on cuda:{t.device.index}, the current device is cuda:{dev}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name}: {have} bytes, the call needs at least {nbytes}")
     return t.data_ptr()
+
+
+def _shape2(t, name):
+    if t is None or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D tensor")
+    return int(t.shape[0]), int(t.shape[1])
 
 
 def _stream(stream):
@@ -247,10 +271,17 @@ def w4a16_prepare_weights(W_bits, group=GROUP):
 
 
 # ---------------------------------------------------------------- device --
+#
+# Every wrapper checks, before calling into the library, that each tensor
+# covers the extent the call will read or write for the sizes it passes (the
+# library sees only pointers and sizes), and that each tensor is on the
+# current device.
 
 def svdq_channel_absmax(X, absmax, stream=None):
-    M, K = X.shape
-    st = lib().svdq_channel_absmax(_dev_ptr(X, 2), M, K, _dev_ptr(absmax, 4), _stream(stream))
+    M, K = _shape2(X, "X")
+    dev = _current_device()
+    st = lib().svdq_channel_absmax(_dev_ptr(X, 2, M * K * 2, "X", dev), M, K,
+                                   _dev_ptr(absmax, 4, K * 4, "absmax", dev), _stream(stream))
     _check("svdq_channel_absmax", st)
 
 
@@ -258,26 +289,44 @@ def svdq_act_workspace_bytes(M, K, rank) -> int:
     return int(lib().svdq_act_workspace_bytes(M, K, rank))
 
 
-def _ws(workspace):
-    return (None, 0) if workspace is None else (_dev_ptr(workspace), workspace.numel() * workspace.element_size())
+def _ws(workspace, dev):
+    if workspace is None:
+        return None, 0
+    return _dev_ptr(workspace, None, 0, "workspace", dev), workspace.numel() * workspace.element_size()
 
 
 def svdq_quantize_act(X, smooth, l1t, qx, sx, T, rank, group=GROUP, qfmt=QFMT_INT4, workspace=None,
                       stream=None):
-    M, K = X.shape
-    wp, wb = _ws(workspace)
-    st = lib().svdq_quantize_act(_dev_ptr(X, 2), _dev_ptr(smooth, 4), _dev_ptr(l1t, 2), M, K, rank,
-                                 group, qfmt, _dev_ptr(qx, 1), _dev_ptr(sx, 4), _dev_ptr(T, 2),
-                                 wp, wb, _stream(stream))
+    M, K = _shape2(X, "X")
+    dev = _current_device()
+    G = K // group if group > 0 else 0
+    wp, wb = _ws(workspace, dev)
+    st = lib().svdq_quantize_act(
+        _dev_ptr(X, 2, M * K * 2, "X", dev), _dev_ptr(smooth, 4, K * 4, "smooth", dev),
+        _dev_ptr(l1t, 2, rank * K * 2, "l1t", dev), M, K, rank, group, qfmt,
+        _dev_ptr(qx, 1, M * svdq_qrow_bytes(K, qfmt), "qx", dev), _dev_ptr(sx, 4, G * M * 4, "sx", dev),
+        _dev_ptr(T, 2, M * rank * 2, "T", dev), wp, wb, _stream(stream))
     _check("svdq_quantize_act", st)
+
+
+def _linear_operands(qx, sx, T, qw, sw, l2t, bias, M, N, K, rank, group, qfmt, dev):
+    """Checked pointers of the W4A4 GEMM's inputs (shared by the linear and
+    the fused MLP entry point)."""
+    R = svdq_qrow_bytes(K, qfmt)
+    G = K // group if group > 0 else 0
+    return (_dev_ptr(qx, 1, M * R, "qx", dev), _dev_ptr(sx, 4, G * M * 4, "sx", dev),
+            _dev_ptr(T, 2, M * rank * 2, "T", dev), _dev_ptr(qw, 1, N * R, "qw", dev),
+            _dev_ptr(sw, 4, G * N * 4, "sw", dev), _dev_ptr(l2t, 2, N * rank * 2, "l2t", dev),
+            _dev_ptr(bias, 2, N * 2, "bias", dev))
 
 
 def svdq_w4a4_linear(qx, sx, T, qw, sw, l2t, bias, Y, M, N, K, rank, group=GROUP, qfmt=QFMT_INT4,
                      stream=None):
+    dev = _current_device()
     y_dtype = SVDQ_F32 if Y.element_size() == 4 else SVDQ_BF16
-    st = lib().svdq_w4a4_linear(_dev_ptr(qx, 1), _dev_ptr(sx, 4), _dev_ptr(T, 2), _dev_ptr(qw, 1),
-                                _dev_ptr(sw, 4), _dev_ptr(l2t, 2), _dev_ptr(bias, 2), M, N, K, rank,
-                                group, qfmt, _dev_ptr(Y), y_dtype, _stream(stream))
+    ins = _linear_operands(qx, sx, T, qw, sw, l2t, bias, M, N, K, rank, group, qfmt, dev)
+    st = lib().svdq_w4a4_linear(*ins, M, N, K, rank, group, qfmt,
+                                _dev_ptr(Y, None, M * N * Y.element_size(), "Y", dev), y_dtype, _stream(stream))
     _check("svdq_w4a4_linear", st)
 
 
@@ -288,17 +337,25 @@ def svdq_mlp_workspace_bytes(M, N, rank_down) -> int:
 def svdq_w4a4_linear_gelu_quantize(qx, sx, T, qw, sw, l2t, bias, M, N, K, rank, smooth_down, l1t_down,
                                    rank_down, qx_down, sx_down, T_down, Y_up=None, workspace=None,
                                    group=GROUP, stream=None):
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dev = _current_device()
+    ins = _linear_operands(qx, sx, T, qw, sw, l2t, bias, M, N, K, rank, group, QFMT_FP6, dev)
+    Gd = N // group if group > 0 else 0
+    ws_need = svdq_mlp_workspace_bytes(M, N, rank_down)
     st = lib().svdq_w4a4_linear_gelu_quantize(
-        _dev_ptr(qx, 1), _dev_ptr(sx, 4), _dev_ptr(T, 2), _dev_ptr(qw, 1), _dev_ptr(sw, 4), _dev_ptr(l2t, 2),
-        _dev_ptr(bias, 2), M, N, K, rank, group, _dev_ptr(smooth_down, 4), _dev_ptr(l1t_down, 2), rank_down,
-        _dev_ptr(qx_down, 1), _dev_ptr(sx_down, 4), _dev_ptr(T_down, 2), _dev_ptr(Y_up, 2),
-        _dev_ptr(workspace), ws_bytes, _stream(stream))
+        *ins, M, N, K, rank, group, _dev_ptr(smooth_down, 4, N * 4, "smooth_down", dev),
+        _dev_ptr(l1t_down, 2, rank_down * N * 2, "l1t_down", dev), rank_down,
+        _dev_ptr(qx_down, 1, M * svdq_qrow_bytes(N, QFMT_FP6), "qx_down", dev),
+        _dev_ptr(sx_down, 4, Gd * M * 4, "sx_down", dev), _dev_ptr(T_down, 2, M * rank_down * 2, "T_down", dev),
+        _dev_ptr(Y_up, 2, M * N * 2, "Y_up", dev), _dev_ptr(workspace, None, ws_need, "workspace", dev),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
     _check("svdq_w4a4_linear_gelu_quantize", st)
 
 
 def svdq_debug_gelu_bf16(y, g, stream=None):
-    st = lib().svdq_debug_gelu_bf16(_dev_ptr(y, 2), _dev_ptr(g, 2), y.numel(), _stream(stream))
+    dev = _current_device()
+    n = y.numel()
+    st = lib().svdq_debug_gelu_bf16(_dev_ptr(y, 2, n * 2, "y", dev), _dev_ptr(g, 2, n * 2, "g", dev), n,
+                                    _stream(stream))
     _check("svdq_debug_gelu_bf16", st)
 
 
@@ -307,47 +364,69 @@ def w8a8_workspace_bytes(M, K) -> int:
 
 
 def w8a8_linear(X, qw, sw, bias, workspace, Y, stream=None):
-    M, K = X.shape
-    N = qw.shape[0]
-    st = lib().w8a8_linear(_dev_ptr(X, 2), _dev_ptr(qw, 1), float(sw), _dev_ptr(bias, 2), M, N, K,
-                           _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
-                           _dev_ptr(Y, 2), _stream(stream))
+    M, K = _shape2(X, "X")
+    N, Kw = _shape2(qw, "qw")
+    if Kw != K:
+        raise ValueError(f"qw has {Kw} columns, X has K = {K}")
+    dev = _current_device()
+    ws_need = w8a8_workspace_bytes(M, K)
+    st = lib().w8a8_linear(_dev_ptr(X, 2, M * K * 2, "X", dev), _dev_ptr(qw, 1, N * K, "qw", dev), float(sw),
+                           _dev_ptr(bias, 2, N * 2, "bias", dev), M, N, K,
+                           _dev_ptr(workspace, None, ws_need, "workspace", dev),
+                           workspace.numel() * workspace.element_size(),
+                           _dev_ptr(Y, 2, M * N * 2, "Y", dev), _stream(stream))
     _check("w8a8_linear", st)
 
 
 def svdq_mx_quantize_act(X, smooth, l1t, qx, ux, T, rank, workspace=None, stream=None):
-    M, K = X.shape
-    wp, wb = _ws(workspace)
-    st = lib().svdq_mx_quantize_act(_dev_ptr(X, 2), _dev_ptr(smooth, 4), _dev_ptr(l1t, 2), M, K, rank,
-                                    _dev_ptr(qx, 1), _dev_ptr(ux, 1), _dev_ptr(T, 2), wp, wb, _stream(stream))
+    M, K = _shape2(X, "X")
+    dev = _current_device()
+    wp, wb = _ws(workspace, dev)
+    st = lib().svdq_mx_quantize_act(
+        _dev_ptr(X, 2, M * K * 2, "X", dev), _dev_ptr(smooth, 4, K * 4, "smooth", dev),
+        _dev_ptr(l1t, 2, rank * K * 2, "l1t", dev), M, K, rank, _dev_ptr(qx, 1, M * (K // 2), "qx", dev),
+        _dev_ptr(ux, 1, (K // 32) * svdq_mx_scale_ld(M), "ux", dev), _dev_ptr(T, 2, M * rank * 2, "T", dev),
+        wp, wb, _stream(stream))
     _check("svdq_mx_quantize_act", st)
 
 
 def svdq_mx_linear(qx, ux, T, qw, uw, l2t, bias, Y, M, N, K, rank, stream=None):
+    dev = _current_device()
     y_dtype = SVDQ_F32 if Y.element_size() == 4 else SVDQ_BF16
-    st = lib().svdq_mx_linear(_dev_ptr(qx, 1), _dev_ptr(ux, 1), _dev_ptr(T, 2), _dev_ptr(qw, 1), _dev_ptr(uw, 1),
-                              _dev_ptr(l2t, 2), _dev_ptr(bias, 2), M, N, K, rank, _dev_ptr(Y), y_dtype,
-                              _stream(stream))
+    st = lib().svdq_mx_linear(
+        _dev_ptr(qx, 1, M * (K // 2), "qx", dev), _dev_ptr(ux, 1, (K // 32) * svdq_mx_scale_ld(M), "ux", dev),
+        _dev_ptr(T, 2, M * rank * 2, "T", dev), _dev_ptr(qw, 1, N * (K // 2), "qw", dev),
+        _dev_ptr(uw, 1, (K // 32) * svdq_mx_scale_ld(N), "uw", dev), _dev_ptr(l2t, 2, N * rank * 2, "l2t", dev),
+        _dev_ptr(bias, 2, N * 2, "bias", dev), M, N, K, rank,
+        _dev_ptr(Y, None, M * N * Y.element_size(), "Y", dev), y_dtype, _stream(stream))
     _check("svdq_mx_linear", st)
 
 
 def w4a16_linear(X, packed, bias, Y, N, group=GROUP, stream=None):
     """Y [M, N] bf16 = X [M, K] bf16 times the W4A16 container `packed`."""
-    M, K = X.shape
-    st = lib().w4a16_linear(_dev_ptr(X, 2), _dev_ptr(packed, 1), _dev_ptr(bias, 2), M, N, K, group,
-                            _dev_ptr(Y, 2), _stream(stream))
+    M, K = _shape2(X, "X")
+    dev = _current_device()
+    st = lib().w4a16_linear(_dev_ptr(X, 2, M * K * 2, "X", dev),
+                            _dev_ptr(packed, 1, w4a16_weight_bytes(K, N), "packed", dev),
+                            _dev_ptr(bias, 2, N * 2, "bias", dev), M, N, K, group,
+                            _dev_ptr(Y, 2, M * N * 2, "Y", dev), _stream(stream))
     _check("w4a16_linear", st)
 
 
 def svdq_debug_group_partials(qx, qw, P, M, N, K, group=GROUP, qfmt=QFMT_INT4, stream=None):
-    st = lib().svdq_debug_group_partials(_dev_ptr(qx, 1), _dev_ptr(qw, 1), M, N, K, group, qfmt,
-                                         _dev_ptr(P, 4), _stream(stream))
+    dev = _current_device()
+    R = svdq_qrow_bytes(K, qfmt)
+    G = K // group if group > 0 else 0
+    st = lib().svdq_debug_group_partials(_dev_ptr(qx, 1, M * R, "qx", dev), _dev_ptr(qw, 1, N * R, "qw", dev),
+                                         M, N, K, group, qfmt, _dev_ptr(P, 4, G * M * N * 4, "P", dev),
+                                         _stream(stream))
     _check("svdq_debug_group_partials", st)
 
 
 def w8a8_debug_acc(qx, qw, acc, M, N, K, stream=None):
-    st = lib().w8a8_debug_acc(_dev_ptr(qx, 1), _dev_ptr(qw, 1), M, N, K, _dev_ptr(acc, 4),
-                              _stream(stream))
+    dev = _current_device()
+    st = lib().w8a8_debug_acc(_dev_ptr(qx, 1, M * K, "qx", dev), _dev_ptr(qw, 1, N * K, "qw", dev), M, N, K,
+                              _dev_ptr(acc, 4, M * N * 4, "acc", dev), _stream(stream))
     _check("w8a8_debug_acc", st)
 
 

@@ -1,8 +1,8 @@
 // C-ABI layer of libsvdq.so: argument validation, the fail-closed device
 // check and launch dispatch. Every check runs before anything is launched, so
-// a rejected call writes nothing ("clear error instead of an incorrect
-// result": "Hugging Face встроила Nunchaku в Diffusers..." (iitog.ru),
-// hardware paragraph).
+// a rejected call writes nothing: an unsupported device or argument fails
+// closed with a status instead of producing output ("Hugging Face встроила
+// Nunchaku в Diffusers..." (iitog.ru), hardware paragraph).
 
 #include "svdq.h"
 #include "internal.h"

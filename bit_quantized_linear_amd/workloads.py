@@ -135,17 +135,6 @@ def mlp_down_bias() -> dict:
     return bias(MLP_DOWN, seed_offset=8)
 
 
-def gelu_bf16(y: np.ndarray) -> dict:
-    """erf-GELU of a float array, rounded to bf16: the MLP's activation between
-    its two projections, applied on the host to build the second input."""
-    from scipy.special import erf
-
-    y = np.asarray(y, dtype=np.float64)
-    g = (0.5 * y * (1.0 + erf(y / np.sqrt(2.0)))).astype(np.float32)
-    bits = bf16_bits_from_f32(g)
-    return {"bits": bits, "values": f32_from_bf16_bits(bits)}
-
-
 def random_bf16(seed: int, shape, std: float = 1.0) -> dict:
     """Plain N(0, std) bf16 array for edge-case tests."""
     x = _normal(seed, shape, std)

@@ -287,6 +287,18 @@ def main_product(qx, sx, qw, sw, group=GROUP):
     return y
 
 
+def main_product_dense(qx, sx, qw, sw, group=GROUP):
+    """y_main = dequant(qx) @ dequant(qw): the dequantize-then-matmul closed
+    form of main_product, one float64 matmul over all of K. Every product
+    sx qx sw qw is exact to 2^-53 and the K-term sum carries float64 rounding
+    only, so it agrees with main_product to far below fp32 resolution; it is
+    what full-size comparisons use (one multithreaded matmul instead of a
+    loop of G matmuls and elementwise passes)."""
+    Xd = dequantize(qx, sx, group)
+    Wd = dequantize(np.asarray(qw).T, sw, group)
+    return Xd @ Wd.T
+
+
 def linear_from_parts(qx, sx, T, qw, sw, L2, bias=None, group=GROUP):
     """y = sum_g sx sw P + T L2 + bias, float64 (before the output rounding)."""
     y = main_product(qx, sx, qw, sw, group)
@@ -332,6 +344,19 @@ def forward(X, prep, bias=None, out_dtype="bf16", group=GROUP):
     qx, sx = quantize_activations(X, prep["s"], group)
     T = lowrank_down(X, prep["L1s"])
     y64 = linear_from_parts(qx, sx, T, prep["qw"], prep["sw"], prep["L2"], bias, group)
+    return {"qx": qx, "sx": sx, "T": T, "y64": y64, "y": round_output(y64, out_dtype)}
+
+
+def forward_dense(X, prep, bias=None, out_dtype="bf16", group=GROUP):
+    """forward with the main product in its closed form (main_product_dense);
+    the same stages otherwise."""
+    qx, sx = quantize_activations(X, prep["s"], group)
+    T = lowrank_down(X, prep["L1s"])
+    y64 = main_product_dense(qx, sx, prep["qw"], prep["sw"], group)
+    if T.size and np.asarray(prep["L2"]).size:
+        y64 += T @ np.asarray(prep["L2"], dtype=F64)
+    if bias is not None:
+        y64 += np.asarray(bias, dtype=F64)[None, :]
     return {"qx": qx, "sx": sx, "T": T, "y64": y64, "y": round_output(y64, out_dtype)}
 
 

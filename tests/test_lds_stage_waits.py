@@ -3,10 +3,12 @@ its own LDS variable so that the compiler can tell the stage being refilled
 from the one being read. With the stages in one array, in a kernel with
 more than one LDS variable, it put a wait for every outstanding load
 (`s_waitcnt vmcnt(0)`) between a stage's refill loads and its first LDS
-read, so each stage waited for loads it had just issued. This compiles the three kernels to gfx950 assembly (host only, no
-GPU) and checks that no such wait sits between a direct-to-LDS load and the
-next LDS read unless a barrier separates them (the intended waits come
-right before the barrier that ends a stage, or the one after the prologue).
+read, so each stage waited for loads it had just issued. This compiles the
+three kernels to gfx950 assembly (host only, no GPU) and checks that no wait
+that needs one of a stage's direct-to-LDS loads to have landed sits between
+those loads and the next LDS read unless a barrier separates them (the
+intended waits come right before the barrier that ends a stage, or the one
+after the prologue).
 """
 
 import os
@@ -37,28 +39,33 @@ def _assembly(src, tmp_path):
 
 
 def _stalls(lines):
-    """(line, text) of every vmcnt(0) wait found after a direct-to-LDS load
-    and before the next LDS read, with no barrier and no load into registers
-    in between (text order)."""
+    """(line, text) of every wait on the vector-memory counter that makes an
+    LDS read wait for direct-to-LDS loads of the current stage: after n such
+    loads (counted since the last barrier, with no load into registers after
+    them), a `vmcnt(c)` with c < n can only be passed once n - c of them have
+    landed, so if an LDS read follows before the next barrier, that read
+    waits for the refill (text order; the loads return in issue order)."""
     found = []
-    pending_lds_load = False
+    lds_loads = 0
     wait_line = None
     for i, raw in enumerate(lines):
         line = raw.strip()
         if line.endswith(":") or line.startswith(".") and not line.startswith(".LBB"):
             continue
         if re.match(r"(buffer|global)_load\S*\s.*\blds\b", line):
-            pending_lds_load, wait_line = True, None
+            lds_loads += 1
         elif re.match(r"(buffer|global|flat)_load", line) or line.startswith("s_barrier") or \
                 line.startswith("s_endpgm"):
             # a load into registers: a later wait may be for it (the epilogue's
             # low-rank operands); a barrier ends the stage
-            pending_lds_load, wait_line = False, None
-        elif pending_lds_load and line.startswith("s_waitcnt") and re.search(r"vmcnt\(0\)", line):
-            wait_line = (i + 1, line)
+            lds_loads, wait_line = 0, None
+        elif lds_loads and line.startswith("s_waitcnt"):
+            m = re.search(r"vmcnt\((\d+)\)", line)
+            if m and int(m.group(1)) < lds_loads:
+                wait_line = (i + 1, line)
         elif line.startswith("ds_read") and wait_line is not None:
             found.append(wait_line)
-            pending_lds_load, wait_line = False, None
+            lds_loads, wait_line = 0, None
     return found
 
 
@@ -77,6 +84,14 @@ def test_checker_flags_the_stalling_pattern():
                 "s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)", "s_barrier", "ds_read_b128 v[8:11], v3"]
     epilogue = ["buffer_load_dwordx4 v2, s[4:7], 0 offen lds", "global_load_dwordx4 v[4:7], v[0:1], off",
                 "s_waitcnt vmcnt(0)", "ds_read_b128 v[8:11], v3"]
+    # a partial wait after a stage's refill loads stalls the reads just the same
+    partial = ["buffer_load_dwordx4 v2, s[4:7], 0 offen lds"] * 8 + ["s_waitcnt vmcnt(3)",
+                                                                       "ds_read_b128 v[8:11], v3"]
+    # ...while a wait that leaves all of them in flight does not
+    harmless = ["buffer_load_dwordx4 v2, s[4:7], 0 offen lds"] * 4 + ["s_waitcnt vmcnt(4)",
+                                                                        "ds_read_b128 v[8:11], v3"]
     assert _stalls(bad) == [(2, "s_waitcnt vmcnt(0)")]
+    assert _stalls(partial) == [(9, "s_waitcnt vmcnt(3)")]
+    assert _stalls(harmless) == []
     assert _stalls(good_end) == []
     assert _stalls(epilogue) == []

@@ -162,6 +162,29 @@ def test_main_product_equals_dequantize_then_matmul():
             assert P[g, m, n] == want
 
 
+def test_dense_closed_form_agrees_with_the_group_loop():
+    """main_product_dense and forward_dense (used at full size) against the
+    group loop: within float64 rounding of the largest term sum, identical
+    codes, scales and T, and the same rounded output except where y64 lies
+    within that rounding of an output rounding boundary (none here)."""
+    X, W, b, r = _tiny_problem(M=70, K=320, N=48, r=16, seed=5)
+    prep = sq.prepare_weights(W, sq.channel_absmax(X), r)
+    qx, sx = sq.quantize_activations(X, prep["s"])
+    loop = sq.main_product(qx, sx, prep["qw"], prep["sw"])
+    dense = sq.main_product_dense(qx, sx, prep["qw"], prep["sw"])
+    scale = np.abs(sq.dequantize(qx, sx)) @ np.abs(sq.dequantize(prep["qw"].T, prep["sw"]).T)
+    assert np.all(np.abs(loop - dense) <= 1e-13 * scale)
+    for out in ("f32", "bf16"):
+        a = sq.forward(X, prep, b, out)
+        d = sq.forward_dense(X, prep, b, out)
+        for k in ("qx", "sx", "T"):
+            assert np.array_equal(a[k], d[k]), k
+        assert np.array_equal(a["y"], d["y"])
+    # a dropped group in either form would show
+    bad = sq.main_product(qx[:, 64:], sx[1:], prep["qw"][64:], prep["sw"][1:])
+    assert np.abs(bad - dense).max() > 1e3 * np.abs(loop - dense).max()
+
+
 def test_full_rank_identity():
     """With r = min(K, N) and unrounded factors the residual vanishes and the
     linear is X W + bias. Catches: s applied the wrong way round, 1/s not
