@@ -79,6 +79,13 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m bit_quantized_linear_amd.build` (there is no CPU fallback)")
+        # one HIP runtime per process: torch (the device memory and stream
+        # plumbing) is loaded first, so that this library binds to the HIP
+        # runtime torch already uses instead of loading a second one beside it
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         handle = C.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)

@@ -11,8 +11,14 @@
 //   acc[m, n] += fp32(sx[g, m] sw[g, n]) * P[g, m, n]     (fp32, g ascending)
 //   y = acc + T L2 + bias  ->  bf16 (nearest even) or fp32
 //
-// The nibbles are unpacked to 16 * code, so the MFMA sums 256 * P; the factor
-// 1/256 is folded into the activation scale (exact power-of-two scaling).
+// The nibbles are unpacked to 16 * code, so the MFMA sums 256 * P. The main
+// loop accumulates acc' = sum_g fp32(sx sw) (256 P) -- 256 times the fp32
+// accumulator of the formula above at every step, since a power-of-two factor
+// commutes with each rounding -- and acc = acc' / 256 is taken once before the
+// low-rank branch is added. The scale product is rounded where the formula
+// rounds it, also for groups so small that it is a subnormal fp32 (folding
+// 1/256 into the scale instead would push such products 8 binades further
+// into the subnormal range and lose their precision).
 
 #include <hip/hip_runtime.h>
 
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void w4a4_gemm_kernel(
             // the column is the token m = r32
             float sxm[2];
 #pragma unroll
-            for (int im = 0; im < 2; ++im) sxm[im] = cur.sb[wm * 64 + im * 32 + r32] * (1.0f / 256.0f);
+            for (int im = 0; im < 2; ++im) sxm[im] = cur.sb[wm * 64 + im * 32 + r32];
 #pragma unroll
             for (int in = 0; in < 2; ++in) {
 #pragma unroll
@@ -120,6 +126,15 @@ __global__ __launch_bounds__(kGemmThreads, 2) void w4a4_gemm_kernel(
     }
 
     if constexpr (kEpi == W4Epilogue::kLinear) {
+        // acc = acc' / 256 (exact while acc is a normal fp32 number; a result
+        // in the subnormal range is rounded once more, by at most half of
+        // 2^-149)
+#pragma unroll
+        for (int in = 0; in < 2; ++in)
+#pragma unroll
+            for (int im = 0; im < 2; ++im)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[in][im][e] *= 1.0f / 256.0f;
         // low-rank up-projection: C^T += L2^T-rows (A, weight side) x T-rows
         // (B, token side) on bf16 MFMA, K = rank in slices of 16
         for (int kk = 0; kk < rank; kk += 16) {

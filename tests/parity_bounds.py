@@ -11,11 +11,16 @@ a handful of them through.
 W4A4 (reading R12 order: main + low-rank + bias, one output rounding):
   y32 = fl(sum_g fl(sx sw) P_g + sum_j T_j L2_j + bias) in fp32, so
   |y32 - y64| <= c u (sum_g |sx sw P_g| + sum_j |T_j L2_j| + |bias|) + c 2^-149
+  + 2^-150 sum_g |P_g|
   with u = 2^-24 and c = 2 (G + r + 3) (one rounding per scale product, per
   group accumulation, per low-rank product sum, and the bias add, doubled to
   cover the matrix core's internal accumulation order; the absolute term
-  covers results in fp32's subnormal range). The term sum is bounded by
-  Cauchy-Schwarz: sum_g |sx sw P_g| <= ||dequant(qx)[m]|| ||dequant(qw)[:, n]||.
+  covers results in fp32's subnormal range). The last term is the scale
+  product fl(sx sw) rounded in fp32's subnormal range, where its error is
+  absolute (at most half of 2^-149) and is multiplied by the group partial.
+  The sums are bounded by Cauchy-Schwarz:
+  sum_g |sx sw P_g| <= ||dequant(qx)[m]|| ||dequant(qw)[:, n]|| and
+  sum_g |P_g| <= ||qx[m]|| ||qw[:, n]||.
   When the device's T differs from the oracle's (within its own checked
   bound), sum_j |dT_j| |L2_j| is added.
   The output rounding adds one unit in the last place of the output type at
@@ -62,7 +67,9 @@ def w4a4_tolerance(qx, sx, qw, sw, T, L2, bias, got, ref, out, dT=None):
     if bias is not None:
         S = S + np.abs(np.asarray(bias, dtype=F64))[None, :]
     c = 2.0 * (G + r + 3)
-    tol = c * U32 * S + c * F32_TINY
+    cx = np.linalg.norm(np.asarray(qx, dtype=F64), axis=1)
+    cw = np.linalg.norm(np.asarray(qw, dtype=F64), axis=0)
+    tol = c * U32 * S + c * F32_TINY + 0.5 * F32_TINY * cx[:, None] * cw[None, :]
     if dT is not None and r:
         tol = tol + np.abs(np.asarray(dT, dtype=F64)) @ np.abs(np.asarray(L2, dtype=F64))
     big = np.maximum(np.abs(np.asarray(got, dtype=F64)), np.abs(np.asarray(ref, dtype=F64)))

@@ -121,7 +121,12 @@ def _calls():
     }
 
 
-CALLS = sorted(_calls())
+CALLS = ["channel_absmax", "gelu", "gelu_quantize", "group_partials", "mx_linear", "mx_quantize_act",
+         "quantize_act", "w4a16_linear", "w4a4_linear", "w8a8_acc", "w8a8_linear"]
+
+
+def test_the_call_list_is_complete():
+    assert sorted(_calls()) == CALLS
 
 
 @pytest.mark.parametrize("call", CALLS)

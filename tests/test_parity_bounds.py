@@ -98,3 +98,46 @@ def test_w8a8_bound():
     tol = PB.w8a8_tolerance(ref["acc"], ref["sx"], sw, bias, bad, ref["y"])
     with pytest.raises(AssertionError, match="outside the bound"):
         PB.check_elementwise(bad, ref["y"], tol)
+
+
+def test_subnormal_scale_products_stay_inside_the_bound(problem):
+    """Rows scaled far down (2^-120): fl(sx sw) falls into fp32's subnormal
+    range, where its rounding error is absolute; the fp32 emulation must
+    still be inside the bound."""
+    X, prep, bias = problem
+    Xs = X.copy()
+    Xs[2] *= 2.0 ** -120
+    Xs[5] *= 2.0 ** -110
+    ref = sq.forward(Xs, prep, None, "f32")
+    prod = ref["sx"][:, 2][:, None].astype(F64) * prep["sw"].astype(F64)
+    assert np.any((prod > 0) & (prod < 2.0 ** -126))
+    got = emulate_w4a4(ref["qx"], ref["sx"], prep["qw"], prep["sw"], ref["T"], prep["L2"], None, "f32")
+    tol = PB.w4a4_tolerance(ref["qx"], ref["sx"], prep["qw"], prep["sw"], ref["T"], prep["L2"], None, got,
+                            ref["y"], "f32")
+    PB.check_elementwise(got, ref["y"], tol)
+
+
+def test_scale_folded_with_the_unpack_factor_falls_outside_for_tiny_rows(problem):
+    """A device that folds the 1/256 of the 16 * code nibble unpack into the
+    activation scale (fl(fl(sx / 256) sw) times 256 P) pushes the scale
+    products of tiny rows 8 binades deeper into fp32's subnormal range; the
+    bound flags it, while the product rounded where the formula rounds it
+    passes (test above)."""
+    X, prep, bias = problem
+    Xs = X.copy()
+    Xs[2] *= 2.0 ** -120
+    ref = sq.forward(Xs, prep, None, "f32")
+    M, K = ref["qx"].shape
+    acc = np.zeros((M, prep["qw"].shape[1]))
+    for g in range(K // 64):
+        sl = slice(64 * g, 64 * g + 64)
+        P = ref["qx"][:, sl].astype(F64) @ prep["qw"][sl].astype(F64)
+        C = rn32(rn32(ref["sx"][g].astype(F64) / 256)[:, None] * prep["sw"][g][None, :].astype(F64))
+        acc = rn32(C * (256 * P) + acc)
+    for j in range(ref["T"].shape[1]):
+        acc = rn32(acc + ref["T"][:, j:j + 1] * prep["L2"][j:j + 1, :])
+    got = sq.round_output(acc, "f32")
+    tol = PB.w4a4_tolerance(ref["qx"], ref["sx"], prep["qw"], prep["sw"], ref["T"], prep["L2"], None, got,
+                            ref["y"], "f32")
+    with pytest.raises(AssertionError, match="outside the bound"):
+        PB.check_elementwise(got, ref["y"], tol)
