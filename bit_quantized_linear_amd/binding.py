@@ -44,6 +44,7 @@ SIGNATURES = {
     "svdq_channel_absmax": (_i, [_vp, _i, _i, _vp, _vp]),
     "svdq_act_workspace_bytes": (_sz, [_i, _i, _i]),
     "svdq_quantize_act": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "svdq_quantize_act_noalloc": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "svdq_w4a4_linear": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
     "svdq_mlp_workspace_bytes": (_sz, [_i, _i, _i]),
     "svdq_w4a4_linear_gelu_quantize": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _i,
@@ -314,6 +315,20 @@ def svdq_quantize_act(X, smooth, l1t, qx, sx, T, rank, group=GROUP, qfmt=QFMT_IN
         _dev_ptr(qx, 1, M * svdq_qrow_bytes(K, qfmt), "qx", dev), _dev_ptr(sx, 4, G * M * 4, "sx", dev),
         _dev_ptr(T, 2, M * rank * 2, "T", dev), wp, wb, _stream(stream))
     _check("svdq_quantize_act", st)
+
+
+def svdq_quantize_act_noalloc(X, smooth, l1t, qx, sx, T, rank, group=GROUP, qfmt=QFMT_INT4, stream=None):
+    """svdq_quantize_act with the library's fixed device scratch instead of a
+    caller workspace (allocates nothing)."""
+    M, K = _shape2(X, "X")
+    dev = _current_device()
+    G = K // group if group > 0 else 0
+    st = lib().svdq_quantize_act_noalloc(
+        _dev_ptr(X, 2, M * K * 2, "X", dev), _dev_ptr(smooth, 4, K * 4, "smooth", dev),
+        _dev_ptr(l1t, 2, rank * K * 2, "l1t", dev), M, K, rank, group, qfmt,
+        _dev_ptr(qx, 1, M * svdq_qrow_bytes(K, qfmt), "qx", dev), _dev_ptr(sx, 4, G * M * 4, "sx", dev),
+        _dev_ptr(T, 2, M * rank * 2, "T", dev), _stream(stream))
+    _check("svdq_quantize_act_noalloc", st)
 
 
 def _linear_operands(qx, sx, T, qw, sw, l2t, bias, M, N, K, rank, group, qfmt, dev):

@@ -9,6 +9,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 #include "quant_common.h"
@@ -358,6 +360,39 @@ static hipError_t launch_act(const uint16_t *X, const float *smooth, const uint1
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !tpart) return e;
     return launch_tpart_reduce(tpart, kp, M, rank, T, stream);
+}
+
+// Scratch of the allocation-free activation pass (svdq_quantize_act_noalloc):
+// the fp32 partial sums of T, [parts][M][rank], when K is split across
+// blocks. act_k_parts keeps parts x ceil(M / 16) <= 2048 blocks whenever it
+// splits, so parts x M <= 32768 and the partials never exceed 32768 x 64 x 4
+// bytes = 8 MiB. Every element the reduction reads is written by the same
+// call first, so nothing needs clearing; calls that overlap on one device
+// share this array and race.
+static __device__ __align__(256) float scratch[kActScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+float *g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+hipError_t act_scratch_pointer(float **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        // the array's device address on this device (its name in host code
+        // is only a host-side handle)
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<float *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_quantize_act(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M,

@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 constexpr int kMaxDevices = 64;
 
 std::mutex g_mutex;
@@ -242,6 +242,27 @@ svdq_status svdq_quantize_act(const uint16_t *X, const float *smooth,
     return launched(svdq::launch_quantize_act(X, smooth, rank ? l1t : nullptr, M, K, rank, qfmt, qx, sx,
                                               rank ? T : nullptr, static_cast<float *>(workspace),
                                               (hipStream_t)stream));
+}
+
+svdq_status svdq_quantize_act_noalloc(const uint16_t *X, const float *smooth, const uint16_t *l1t, int M,
+                                      int K, int rank, int group, int qfmt, uint8_t *qx, float *sx,
+                                      uint16_t *T, void *stream) {
+    svdq_status st = check_w4a4_shape(M, K, rank, group);
+    if (st != SVDQ_OK) return st;
+    if (qfmt != SVDQ_QFMT_INT4 && qfmt != SVDQ_QFMT_FP6) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (!smooth || (M > 0 && (!X || !qx || !sx))) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (rank > 0 && (!l1t || (M > 0 && !T))) return SVDQ_ERR_INVALID_ARGUMENT;
+    if (svdq::act_workspace_size(M, K, rank) > svdq::kActScratchBytes) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(X) || !aligned16(smooth) || !aligned16(l1t) || !aligned16(qx) || !aligned16(sx) ||
+        !aligned16(T))
+        return SVDQ_ERR_MISALIGNED;
+    st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0) return SVDQ_OK;
+    float *scratch = nullptr;
+    if (svdq::act_scratch_pointer(&scratch) != hipSuccess) return SVDQ_ERR_HIP;
+    return launched(svdq::launch_quantize_act(X, smooth, rank ? l1t : nullptr, M, K, rank, qfmt, qx, sx,
+                                              rank ? T : nullptr, scratch, (hipStream_t)stream));
 }
 
 size_t svdq_mlp_workspace_bytes(int M, int N, int rank_down) {

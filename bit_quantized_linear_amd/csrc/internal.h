@@ -40,6 +40,11 @@ hipError_t launch_channel_absmax(const uint16_t *X, int M, int K, float *absmax,
 // rank) bytes for T's fp32 partials when K is split across blocks
 int act_k_parts(int M, int K);
 size_t act_workspace_size(int M, int K, int rank);
+// fixed device scratch of svdq_quantize_act_noalloc (bytes; covers
+// act_workspace_size for every supported shape) and its address on the
+// current device, looked up once per device
+constexpr size_t kActScratchBytes = (size_t)8 << 20;
+hipError_t act_scratch_pointer(float **out);
 hipError_t launch_quantize_act(const uint16_t *X, const float *smooth,
                                const uint16_t *l1t, int M, int K, int rank,
                                int qfmt, uint8_t *qx, float *sx, uint16_t *T,

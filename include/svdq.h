@@ -47,7 +47,9 @@
  *  - Only gfx950 is served: any other device gives
  *    SVDQ_ERR_UNSUPPORTED_DEVICE before anything is launched.
  *  - Calls on different streams may run concurrently; the library keeps no
- *    mutable state apart from a per-device architecture cache.
+ *    mutable state apart from a per-device architecture cache and the fixed
+ *    per-device scratch array of svdq_quantize_act_noalloc (the one entry
+ *    point whose concurrent calls on a device must be serialized).
  *
  * Codes lie in [-7, 7] (symmetric grid; -8 never produced); qx and qw hold
  * them in one of two containers (svdq_qformat below). Group scales are fp32,
@@ -293,6 +295,29 @@ svdq_status svdq_quantize_act(const uint16_t *X, const float *smooth,
                               int group, int qfmt, uint8_t *qx, float *sx,
                               uint16_t *T, void *workspace, size_t workspace_bytes,
                               void *stream);
+
+/* svdq_quantize_act without a caller workspace and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments, results and errors as svdq_quantize_act given a workspace (the
+ * same kernels and the same split of K, so the outputs are identical); the
+ * fp32 partial sums of T go to a fixed 8 MiB device array inside the
+ * library (one per device, held until the process ends; its address is
+ * looked up on the first call on each device). Every shape the pass accepts
+ * fits it (when K is split in p parts, p * M <= 32768 and rank <= 64); a
+ * call that would need more is refused with SVDQ_ERR_UNSUPPORTED_SHAPE
+ * before any launch. The array is shared by every call on a device: calls
+ * that overlap in time on one device (different streams, threads or
+ * processes' shared contexts) race on it and must be serialized by the
+ * caller. Nothing in it needs clearing between calls (each call writes
+ * every partial it reads).
+ * Errors: as svdq_quantize_act, and SVDQ_ERR_HIP if the array's address
+ *      cannot be obtained. */
+svdq_status svdq_quantize_act_noalloc(const uint16_t *X, const float *smooth,
+                                      const uint16_t *l1t, int M, int K,
+                                      int rank, int group, int qfmt,
+                                      uint8_t *qx, float *sx, uint16_t *T,
+                                      void *stream);
 
 /* The W4A4 linear with fused low-rank up-projection and bias
  * [HF-SVDQ method and "Nunchaku Lite" paragraph]:

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert b.svdq_version() == 7
+    assert b.svdq_version() == 8
     for s in range(7):
         assert b.status_string(s)
     assert "unknown" in b.status_string(99)
@@ -302,3 +302,29 @@ def test_act_workspace_is_optional_but_checked():
     assert lib.svdq_quantize_act(*args, MISALIGNED, need, None) == b.SVDQ_ERR_MISALIGNED
     assert lib.svdq_mx_quantize_act(FAKE, FAKE, FAKE, 4608, 3072, 32, FAKE, FAKE, FAKE, FAKE, 16, None) == \
         b.SVDQ_ERR_INVALID_ARGUMENT
+
+
+def test_noalloc_scratch_covers_every_split():
+    """The fixed 8 MiB scratch of svdq_quantize_act_noalloc holds T's fp32
+    partials for every shape: the split into p parts keeps p * ceil(M / 16)
+    <= 2048 blocks, so p * M * rank * 4 <= 32768 * 64 * 4 bytes."""
+    worst = 0
+    for M in list(range(1, 33000, 61)) + [4608, 16383, 16384, 16385, 32760, 32768, 65536]:
+        for K in (64, 512, 1024, 3072, 4096, 5120, 12288, 16384, 65536):
+            worst = max(worst, b.svdq_act_workspace_bytes(M, K, 64))
+    assert 0 < worst <= 8 << 20
+
+
+def test_noalloc_entry_point_fails_closed():
+    lib = b.lib()
+    args = lambda M, K, rank, group, qfmt, X=FAKE: (X, FAKE, FAKE, M, K, rank, group, qfmt, FAKE, FAKE, FAKE, None)
+    assert lib.svdq_quantize_act_noalloc(*args(16, 100, 16, 64, 1)) == b.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert lib.svdq_quantize_act_noalloc(*args(16, 128, 24, 64, 1)) == b.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert lib.svdq_quantize_act_noalloc(*args(16, 128, 16, 64, 3)) == b.SVDQ_ERR_INVALID_ARGUMENT
+    assert lib.svdq_quantize_act_noalloc(*args(16, 128, 16, 64, 1, X=None)) == b.SVDQ_ERR_INVALID_ARGUMENT
+    assert lib.svdq_quantize_act_noalloc(*args(16, 128, 16, 64, 1, X=MISALIGNED)) == b.SVDQ_ERR_MISALIGNED
+    b.svdq_debug_set_arch_override("gfx942")
+    try:
+        assert lib.svdq_quantize_act_noalloc(*args(4608, 3072, 32, 64, 1)) == b.SVDQ_ERR_UNSUPPORTED_DEVICE
+    finally:
+        b.svdq_debug_set_arch_override(None)

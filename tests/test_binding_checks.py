@@ -89,6 +89,10 @@ def _calls():
                                                        qfmt=b.QFMT_FP6),
                          {"X": Dev((M, K), 2), "smooth": Dev((K,), 4), "l1t": Dev((R, K), 2),
                           "qx": Dev((M, R6), 1), "sx": Dev((G, M), 4), "T": Dev((M, R), 2)}),
+        "quantize_act_noalloc": (lambda t: b.svdq_quantize_act_noalloc(t["X"], t["smooth"], t["l1t"], t["qx"], t["sx"],
+                                                                       t["T"], R, qfmt=b.QFMT_FP6),
+                                 {"X": Dev((M, K), 2), "smooth": Dev((K,), 4), "l1t": Dev((R, K), 2),
+                                  "qx": Dev((M, R6), 1), "sx": Dev((G, M), 4), "T": Dev((M, R), 2)}),
         "w4a4_linear": (lambda t: b.svdq_w4a4_linear(t["qx"], t["sx"], t["T"], t["qw"], t["sw"], t["l2t"], t["bias"],
                                                      t["Y"], M, N, K, R, qfmt=b.QFMT_FP6),
                         {"qx": Dev((M, R6), 1), "sx": Dev((G, M), 4), "T": Dev((M, R), 2), "qw": Dev((N, R6), 1),
@@ -122,7 +126,7 @@ def _calls():
 
 
 CALLS = ["channel_absmax", "gelu", "gelu_quantize", "group_partials", "mx_linear", "mx_quantize_act",
-         "quantize_act", "w4a16_linear", "w4a4_linear", "w8a8_acc", "w8a8_linear"]
+         "quantize_act", "quantize_act_noalloc", "w4a16_linear", "w4a4_linear", "w8a8_acc", "w8a8_linear"]
 
 
 def test_the_call_list_is_complete():
