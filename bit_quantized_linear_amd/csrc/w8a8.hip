@@ -20,6 +20,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "quant_common.h"
 
 namespace svdq {
 
@@ -69,6 +70,10 @@ __global__ __launch_bounds__(kQThreads) void w8_quantize_kernel(const uint16_t *
     }
     const float sx = __uint_as_float(red[0]) / 127.0f;
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = sx;
+    // x / sx as fp32(double(x) * fp64(1 / sx)): the same value as the IEEE
+    // fp32 division (quotient_fp32). A quotient below 2^-126, where that
+    // argument does not hold, is code 0 either way.
+    const double rsx = sx != 0.0f ? 1.0 / (double)sx : 0.0;
     for (int64_t c = (int64_t)blockIdx.x * kQThreads + threadIdx.x; c < chunks;
          c += (int64_t)gridDim.x * kQThreads) {
         const u32x4 v = *reinterpret_cast<const u32x4 *>(X + c * 8);
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(kQThreads) void w8_quantize_kernel(const uint16_t *
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t h = (i & 1) ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xFFFFu);
-                float r = rintf(bf16_bits_to_f32(h) / sx);  // IEEE division, half-even
+                float r = rintf(quotient_fp32(bf16_bits_to_f32(h), rsx));  // half-even
                 r = fminf(127.0f, fmaxf(-127.0f, r));
                 out[i >> 2] |= ((uint32_t)((int)r) & 0xFFu) << (8 * (i & 3));
             }
