@@ -84,6 +84,8 @@ def parse():
     p.add_argument("--no-mlp", action="store_true")
     p.add_argument("--no-w4a16", action="store_true")
     p.add_argument("--no-mx", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the attention-projection and video configurations")
     p.add_argument("--cpu-rows", type=int, default=4608,
                    help="token rows of the workload the CPU oracle is timed on")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -356,6 +358,146 @@ def cpu_baseline_w4a16(case, X, W, bias):
                       f"M={case.M} K={case.K} N={case.N}"}
 
 
+def w4a4_config_line(name, steps, warmup):
+    """One SVDQuant W4A4 step (activation pass with its workspace + FP6 GEMM)
+    on another configuration of the same layer type, with the library's own
+    preparation: time, TOPS, % of the int8 and FP6 peaks, activation GB/s."""
+    import torch
+
+    from bit_quantized_linear_amd import binding as b
+    from bit_quantized_linear_amd import workloads as wl
+
+    case = wl.CASES[name]
+    M, K, N, r = case.M, case.K, case.N, case.rank
+    X, W, bias = wl.activations(case), wl.weight(case), wl.bias(case)
+    Xd = torch.from_numpy(X["bits"].view(np.int16)).cuda()
+    amax = torch.zeros(K, dtype=torch.float32, device="cuda")
+    b.svdq_channel_absmax(Xd, amax)
+    prep = b.svdq_prepare_weights(W["bits"], amax.cpu().numpy(), r)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+    s_d, l1_d, l2_d, sw_d, b_d = up(prep["s"]), up(prep["l1t"]), up(prep["l2t"]), up(prep["sw"]), up(bias["bits"])
+    qw6 = up(b.svdq_repack_codes(prep["qw"], K, b.QFMT_FP6))
+    qx6 = torch.empty((M, b.svdq_qrow_bytes(K, b.QFMT_FP6)), dtype=torch.uint8, device="cuda")
+    sx = torch.empty((K // 64, M), dtype=torch.float32, device="cuda")
+    T = torch.empty((M, r), dtype=torch.int16, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    ws = torch.empty(max(16, b.svdq_act_workspace_bytes(M, K, r)), dtype=torch.uint8, device="cuda")
+
+    def act():
+        b.svdq_quantize_act(Xd, s_d, l1_d, qx6, sx, T, r, qfmt=b.QFMT_FP6, workspace=ws)
+
+    def gemm():
+        b.svdq_w4a4_linear(qx6, sx, T, qw6, sw_d, l2_d, b_d, Y, M, N, K, r, qfmt=b.QFMT_FP6)
+
+    ms, per, _, each = time_steps([act, gemm], steps, warmup)
+    ops = 2.0 * M * N * K
+    tops, gemm_tops = ops / (ms * 1e-3) / 1e12, ops / (per[1] * 1e-3) / 1e12
+    act_bytes = M * K * 2 + r * K * 2 + K * 4 + M * (K // 4 * 3) + (K // 64) * M * 4 + M * r * 2
+    finite = bool(torch.isfinite(Y.view(torch.bfloat16).float()).all().item())
+    log(f"[bench] {name}: step {ms:.4f} ms (act {per[0]:.4f} ms, gemm {per[1]:.4f} ms) -> {tops:.1f} TOPS")
+    return {"workload": f"{name}: SVDQuant W4A4 linear M={M} K={K} N={N} rank={r} group=64, FP6 container",
+            "ms_per_step": round(ms, 5), "step_ms_median": round(float(np.median(each)), 5),
+            "TOPS": round(tops, 2), "pct_int8_roofline": round(100.0 * tops / INT8_PEAK_TOPS, 2),
+            "act_ms": round(per[0], 5), "act_GB/s": round(act_bytes / (per[0] * 1e-3) / 1e9, 1),
+            "act_frac_hbm": round(act_bytes / (per[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "gemm_ms": round(per[1], 5), "gemm_TOPS": round(gemm_tops, 2),
+            "gemm_pct_int8_roofline": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2),
+            "gemm_frac_fp6_peak": round(gemm_tops / FP6_PEAK_TFLOPS, 4), "outputs_finite": finite}
+
+
+def w8a8_config_line(name, steps, warmup):
+    """The W8A8 tensorwise linear on a configuration (library preparation)."""
+    import torch
+
+    from bit_quantized_linear_amd import binding as b
+    from bit_quantized_linear_amd import workloads as wl
+
+    c8 = wl.CASES[name]
+    X8, W8, b8 = wl.activations(c8), wl.weight(c8), wl.bias(c8)
+    qw8, sw8 = b.w8a8_prepare_weights(W8["bits"])
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+    X8d, qw8d, b8d = up(X8["bits"]), up(qw8), up(b8["bits"])
+    ws = torch.empty(b.w8a8_workspace_bytes(c8.M, c8.K), dtype=torch.uint8, device="cuda")
+    Y8 = torch.empty((c8.M, c8.N), dtype=torch.int16, device="cuda")
+
+    def w8():
+        b.w8a8_linear(X8d, qw8d, sw8, b8d, ws, Y8)
+
+    ms8, _, _, each = time_steps([w8], steps, warmup)
+    ops8 = 2.0 * c8.M * c8.N * c8.K
+    log(f"[bench] {name}: {ms8:.4f} ms")
+    return {"workload": f"{name}: W8A8 tensorwise M={c8.M} K={c8.K} N={c8.N}",
+            "ms": round(ms8, 5), "step_ms_median": round(float(np.median(each)), 5),
+            "TOPS": round(ops8 / (ms8 * 1e-3) / 1e12, 2),
+            "pct_int8_roofline": round(100.0 * ops8 / (ms8 * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)}
+
+
+def measured_peaks():
+    """This chip's matrix-core rates under load (back-to-back MFMAs on every
+    SIMD: FP6 32x32x64, int8 32x32x32, bf16 32x32x16), the shader clock under
+    that load, and the HBM copy bandwidth (a 1 GiB device-to-device copy, read
+    plus write bytes)."""
+    import torch
+
+    from bit_quantized_linear_amd import binding as b
+
+    blocks, iters = 4 * 256, 2000
+    out = torch.empty(8 * blocks, dtype=torch.int64, device="cuda")
+    res = {}
+    for kind, name in ((0, "fp6"), (1, "int8"), (2, "bf16")):
+        b.svdq_debug_mfma_rate(kind, blocks, 50, out)  # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.svdq_debug_mfma_rate(kind, blocks, iters, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        spans = out.view(-1, 2).cpu().numpy().astype(np.float64)
+        clock_mhz = float(np.median(spans[:, 0] / spans[:, 1]) * 100.0)
+        res[name] = {"TOPS": round(b.svdq_debug_mfma_ops(kind, blocks, iters) / (ms * 1e-3) / 1e12, 1),
+                     "shader_clock_MHz": round(clock_mhz, 0)}
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    res["hbm_copy_GB/s"] = round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    log(f"[bench] measured: fp6 {res['fp6']['TOPS']} TOPS, int8 {res['int8']['TOPS']} TOPS, "
+        f"bf16 {res['bf16']['TOPS']} TFLOPS at {res['fp6']['shader_clock_MHz']} MHz; "
+        f"HBM copy {res['hbm_copy_GB/s']} GB/s")
+    return res
+
+
+def cpu_baseline_one_core(case, X, W, bias, rows):
+    """The same oracle forward with its BLAS limited to one thread, on a
+    smaller sample of the same workload (`rows` token rows)."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # noqa: BLE001
+        return None
+    with threadpool_limits(limits=1):
+        res = cpu_baseline(case, X, W, bias, rows)
+    res["cores"] = 1
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -610,6 +752,15 @@ def main():
             out["w8a8"]["cpu_baseline"] = cpu_baseline_w8a8(c8, X8, W8, b8)
             log(f"[bench] w8a8 cpu baseline {out['w8a8']['cpu_baseline']['seconds']:.1f}s")
 
+    if not args.no_configs:
+        # the other configurations of the same layer types: the attention
+        # projection (4608 x 3072 -> 3072) and the video-scale linear (32760 x
+        # 5120 -> 5120, its row tail included), W4A4 and W8A8
+        out["attn_proj"] = w4a4_config_line("attn_proj", args.steps, args.warmup)
+        out["video"] = w4a4_config_line("video", max(5, args.steps // 4), max(2, args.warmup // 2))
+        out["video_w8a8"] = w8a8_config_line("video_w8a8", max(5, args.steps // 4), max(2, args.warmup // 2))
+        torch.cuda.empty_cache()
+
     if not args.no_w4a16:
         c16 = wl.CASES["modulation"]
         X16 = wl.activations(c16)
@@ -680,6 +831,11 @@ def main():
             out["w4a16"]["cpu_baseline"] = cpu_baseline_w4a16(c16, X16, W16, b16)
             log(f"[bench] w4a16 cpu baseline {out['w4a16']['cpu_baseline']['seconds']:.3f}s")
 
+    try:
+        out["measured_peaks"] = measured_peaks()
+    except Exception as e:  # noqa: BLE001 -- reported, never fatal to the bench line
+        out["measured_peaks"] = {"error": str(e)}
+
     out["prepare"] = {"library_s": round(prep_s, 3),
                       "what": "svdq_prepare_weights on the host: smoothing, rank-r SVD, bf16 factors, "
                               "residual, INT4 group codes and scales"}
@@ -687,6 +843,10 @@ def main():
         log(f"[bench] cpu baseline (oracle) on {args.cpu_rows} rows ...")
         out["cpu_baseline"] = cpu_baseline(case, X, W, bias, args.cpu_rows)
         log(f"[bench] cpu baseline {out['cpu_baseline']['seconds']:.1f}s")
+        one = cpu_baseline_one_core(case, X, W, bias, max(64, args.cpu_rows // 16))
+        if one is not None:
+            out["cpu_baseline_one_core"] = one
+            log(f"[bench] cpu baseline, one core: {one['value']:.4f} TOPS ({one['seconds']:.1f}s per pass)")
         from oracle import svdquant as sq
 
         t1 = time.perf_counter()

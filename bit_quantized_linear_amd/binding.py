@@ -62,6 +62,8 @@ SIGNATURES = {
     "svdq_debug_group_partials": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "w8a8_debug_acc": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
     "svdq_debug_set_arch_override": (_i, [C.c_char_p]),
+    "svdq_debug_mfma_ops": (C.c_int64, [_i, _i, _i]),
+    "svdq_debug_mfma_rate": (_i, [_i, _i, _i, _vp, _vp]),
 }
 
 _lib = None
@@ -450,6 +452,19 @@ def w8a8_debug_acc(qx, qw, acc, M, N, K, stream=None):
     st = lib().w8a8_debug_acc(_dev_ptr(qx, 1, M * K, "qx", dev), _dev_ptr(qw, 1, N * K, "qw", dev), M, N, K,
                               _dev_ptr(acc, 4, M * N * 4, "acc", dev), _stream(stream))
     _check("w8a8_debug_acc", st)
+
+
+def svdq_debug_mfma_ops(kind, blocks, iters) -> int:
+    return int(lib().svdq_debug_mfma_ops(kind, blocks, iters))
+
+
+def svdq_debug_mfma_rate(kind, blocks, iters, out, stream=None):
+    """Back-to-back MFMAs of one kind on every SIMD; out: uint64 device tensor
+    of 8 * blocks values (per wave: shader-clock span, real-time span)."""
+    dev = _current_device()
+    st = lib().svdq_debug_mfma_rate(kind, blocks, iters, _dev_ptr(out, 8, 8 * 8 * blocks, "out", dev),
+                                    _stream(stream))
+    _check("svdq_debug_mfma_rate", st)
 
 
 # ------------------------------------------------ convenience allocation --

@@ -317,6 +317,20 @@ svdq_status svdq_debug_gelu_bf16(const uint16_t *y, uint16_t *g, int n, void *st
     return launched(svdq::launch_gelu_bf16(y, g, n, (hipStream_t)stream));
 }
 
+int64_t svdq_debug_mfma_ops(int kind, int blocks, int iters) {
+    if (kind < 0 || kind > 2 || blocks <= 0 || iters <= 0) return 0;
+    return svdq::mfma_rate_ops_per_wave_round(kind) * (int64_t)blocks * 4 * (int64_t)iters;
+}
+
+svdq_status svdq_debug_mfma_rate(int kind, int blocks, int iters, uint64_t *out, void *stream) {
+    if (kind < 0 || kind > 2 || blocks <= 0 || blocks > (1 << 20) || iters <= 0 || !out)
+        return SVDQ_ERR_INVALID_ARGUMENT;
+    if (!aligned16(out)) return SVDQ_ERR_MISALIGNED;
+    const svdq_status st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    return launched(svdq::launch_mfma_rate(kind, blocks, iters, out, (hipStream_t)stream));
+}
+
 svdq_status svdq_w4a4_linear(const uint8_t *qx, const float *sx,
                              const uint16_t *T, const uint8_t *qw,
                              const float *sw, const uint16_t *l2t,

@@ -98,4 +98,8 @@ hipError_t launch_mx_linear(const uint8_t *qx, const uint8_t *ux, const uint16_t
 hipError_t launch_w4a16_linear(const uint16_t *X, const uint8_t *packed, const uint16_t *bias, int M,
                                int N, int K, uint16_t *Y, hipStream_t stream);
 
+// matrix-core rate microbenchmark (peak.hip)
+int64_t mfma_rate_ops_per_wave_round(int kind);
+hipError_t launch_mfma_rate(int kind, int blocks, int iters, uint64_t *out, hipStream_t stream);
+
 }  // namespace svdq

@@ -474,6 +474,19 @@ svdq_status svdq_debug_group_partials(const uint8_t *qx, const uint8_t *qw,
 svdq_status w8a8_debug_acc(const int8_t *qx, const int8_t *qw, int M, int N,
                            int K, int32_t *acc, void *stream);
 
+/* Matrix-core rate on this device, the denominator a roofline fraction can
+ * also be quoted against besides the published peak: `blocks` blocks of 4
+ * waves each run `iters` rounds of 4 independent MFMAs of one kind (kind 0:
+ * FP6 32x32x64 with block scales, 1: int8 32x32x32, 2: bf16 32x32x16) back
+ * to back. out (device, 16-byte aligned, 2 * 4 * blocks uint64 values):
+ * per wave its span in shader-clock cycles and in ticks of the 100 MHz
+ * real-time counter (their ratio is the shader clock under that load).
+ * svdq_debug_mfma_ops gives the operations (2 M N K per MFMA) of such a
+ * launch (0 on a bad argument).
+ * Errors: INVALID_ARGUMENT, MISALIGNED, UNSUPPORTED_DEVICE, HIP. */
+int64_t svdq_debug_mfma_ops(int kind, int blocks, int iters);
+svdq_status svdq_debug_mfma_rate(int kind, int blocks, int iters, uint64_t *out, void *stream);
+
 /* Test hook for the fail-closed path: when `arch` is non-NULL the device
  * check sees that architecture name instead of the real one (NULL restores
  * the real one). Host-only; never launches anything. */

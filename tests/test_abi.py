@@ -328,3 +328,15 @@ def test_noalloc_entry_point_fails_closed():
         assert lib.svdq_quantize_act_noalloc(*args(4608, 3072, 32, 64, 1)) == b.SVDQ_ERR_UNSUPPORTED_DEVICE
     finally:
         b.svdq_debug_set_arch_override(None)
+
+
+def test_mfma_rate_probe_counts_and_fails_closed():
+    # 2 M N K per MFMA, 4 chains, 4 waves per block
+    assert b.svdq_debug_mfma_ops(0, 3, 5) == 2 * 32 * 32 * 64 * 4 * 4 * 3 * 5
+    assert b.svdq_debug_mfma_ops(1, 1, 1) == 2 * 32 * 32 * 32 * 4 * 4
+    assert b.svdq_debug_mfma_ops(2, 1, 1) == 2 * 32 * 32 * 16 * 4 * 4
+    assert b.svdq_debug_mfma_ops(3, 1, 1) == 0 and b.svdq_debug_mfma_ops(0, 0, 1) == 0
+    lib = b.lib()
+    assert lib.svdq_debug_mfma_rate(3, 4, 10, FAKE, None) == b.SVDQ_ERR_INVALID_ARGUMENT
+    assert lib.svdq_debug_mfma_rate(0, 4, 10, None, None) == b.SVDQ_ERR_INVALID_ARGUMENT
+    assert lib.svdq_debug_mfma_rate(0, 4, 10, MISALIGNED, None) == b.SVDQ_ERR_MISALIGNED
