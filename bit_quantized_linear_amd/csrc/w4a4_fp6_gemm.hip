@@ -434,11 +434,18 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
                     __builtin_amdgcn_sched_barrier(0);
                     const i32x8 bm = frag6(cur.b, q * TILE + b16 + im * 32 * GB, q * TILE + b8[im]);
                     const float sxv = cur.sb[q][wm * 64 + im * 32 + r32];
+                    // the slice's MFMAs are issued at raised wave priority
+                    // and its FMAs at the normal one (on a SIMD the MFMAs of
+                    // one wave and the VALU work of others do not overlap;
+                    // letting the waves that are ready for the matrix core go
+                    // first measured 2 % faster)
+                    __builtin_amdgcn_s_setprio(1);
                     const f32x32 C = __builtin_amdgcn_mfma_f32_32x32x1f32(swv, sxv, zero32, 0, 0, 0);
                     const f32x16 P0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bm, zero16, 2, 2, 0,
                                                                                       E8M0_X8, 0, E8M0_X8);
                     const f32x16 P1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bm, zero16, 2, 2, 0,
                                                                                       E8M0_X8, 0, E8M0_X8);
+                    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
                     for (int e = 0; e < 16; ++e) acc[0][im][e] = fmaf(C[e], P0[e], acc[0][im][e]);
 #pragma unroll
