@@ -94,6 +94,12 @@ def parse():
                    help="print the traffic summary from two rocprofv3 --pmc output folders (no GPU)")
     p.add_argument("--pmc-kernel", choices=("fp6_gemm", "w4a16", "mx_gemm"), default="fp6_gemm",
                    help="kernel whose traffic --summarize-pmc reports")
+    p.add_argument("--summarize-trace", metavar="DIR",
+                   help="print per-kernel durations from a rocprofv3 --kernel-trace output folder, one "
+                        "line per kernel and grid shape")
+    p.add_argument("--summarize-counters", nargs="+", metavar=("KERNEL", "DIR"),
+                   help="print a summary of a kernel's SQ/TA/TD/TCC counters from rocprofv3 --pmc "
+                        f"output folders; KERNEL is one of {', '.join(COUNTER_KERNELS)}")
     return p.parse_args()
 
 
@@ -161,6 +167,139 @@ def summarize_pmc(fetch_dir, write_dir, which="fp6_gemm"):
         f"traffic_over_algorithmic: {(fetch_b + write_b) / algo:.3f}",
     ]
     print("\n".join(lines))
+
+
+# Kernels --summarize-counters knows: key in the kernel name, sources whose
+# hash the summary records, the workload, and the MFMA operations one launch
+# must perform (with the counter that counts them), or None.
+COUNTER_KERNELS = {
+    "fp6_gemm": ("w4a4_fp6_kernel<0>", GEMM_SOURCES,
+                 "svdq_w4a4_linear (FP6 container), mlp_up M=4608 K=3072 N=12288 rank=32",
+                 2 * 4608 * 3072 * 12288, "SQ_INSTS_VALU_MFMA_MOPS_F6F4"),
+    "int4_gemm": ("w4a4_gemm_kernel", ("w4a4_gemm.hip", "gemm_int.h", "device_common.h"),
+                  "svdq_w4a4_linear (INT4 container), mlp_up M=4608 K=3072 N=12288 rank=32",
+                  2 * 4608 * 3072 * 12288, "SQ_INSTS_VALU_MFMA_MOPS_I8"),
+    "act": ("quantize_act_kernel<1, 2>", ("act_quant.hip", "quant_common.h", "device_common.h"),
+            "svdq_quantize_act (FP6 container), mlp_up M=4608 K=3072 rank=32", None, None),
+    "mx_gemm": (MX_KERNEL_KEY, MX_SOURCES, "svdq_mx_linear (MXFP4), mlp_up M=4608 K=3072 N=12288 rank=32",
+                2 * 4608 * 3072 * 12288, "SQ_INSTS_VALU_MFMA_MOPS_F6F4"),
+    "w8a8_gemm": ("w8a8_gemm_kernel", ("w8a8.hip", "gemm_int.h", "device_common.h", "quant_common.h"),
+                  "w8a8_linear GEMM, attention projection M=4608 K=3072 N=3072",
+                  2 * 4608 * 3072 * 3072, "SQ_INSTS_VALU_MFMA_MOPS_I8"),
+}
+# grid sizes (work-items) of the workloads above where the kernel also runs
+# at other shapes in the same bench run: the up-projection's 36 x 96 blocks of
+# 256 threads; the activation pass's 288 row tiles x 3 K parts of 512 threads
+COUNTER_GRIDS = {"fp6_gemm": 36 * 96 * 256, "act": 288 * 3 * 512}
+XCDS, CUS, SIMDS = 8, 256, 1024  # MI355X
+
+
+def _dispatch_counters(folder, key, grid=None):
+    """{(folder, dispatch): {counter: value, "_ns": duration}} for the
+    dispatches of the kernel whose name contains `key`, restricted to the
+    given grid size (work-items) or else to the one that occurs most often
+    (the workload named in the summary)."""
+    rows = []
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += [r for r in csv.DictReader(fh) if key in r.get("Kernel_Name", "")]
+    if not rows:
+        raise SystemExit(f"{folder}: no dispatches of {key}")
+    grids = {}
+    for r in rows:
+        grids[r["Grid_Size"]] = grids.get(r["Grid_Size"], 0) + 1
+    grid = str(grid) if grid is not None else max(grids, key=grids.get)
+    out = {}
+    for r in rows:
+        if r["Grid_Size"] != grid:
+            continue
+        d = out.setdefault((folder, r["Dispatch_Id"]), {"_ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out, grid
+
+
+def summarize_counters(which, folders):
+    """Text summary of one kernel's counters (printed to stdout): per-dispatch
+    means of every counter in the folders (one rocprofv3 --pmc pass each) and
+    the figures derived from them. Counter values are totals over the chip
+    (rocprofv3 sums the per-XCD / per-SE instances); GRBM_GUI_ACTIVE counts
+    the dispatch's cycles once per XCD, so its sum over the 8 XCDs is divided
+    by 8. Busy fractions are of every SIMD's (or CU's) cycles over that span."""
+    key, sources, workload, ops, mops_counter = COUNTER_KERNELS[which]
+    lines = [f"# counters of {workload}", f"kernel_source_sha256_16: {gemm_source_hash(sources)}"]
+    derived = []
+    for folder in folders:
+        disp, grid = _dispatch_counters(folder, key, COUNTER_GRIDS.get(which))
+        names = sorted({c for d in disp.values() for c in d if c != "_ns"})
+        mean = {c: sum(d.get(c, 0.0) for d in disp.values()) / len(disp) for c in names + ["_ns"]}
+        lines.append(f"pass {os.path.basename(os.path.normpath(folder))}: {len(disp)} dispatches, grid size {grid}, "
+                     f"{mean['_ns'] / 1e3:.1f} us per dispatch under collection")
+        for c in names:
+            lines.append(f"  {c}: {mean[c]:.0f}")
+        cyc = mean.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+        if not cyc:
+            continue
+        lines.append(f"  kernel_cycles (GRBM_GUI_ACTIVE / {XCDS}): {cyc:.0f} "
+                     f"({cyc / (mean['_ns'] * 1e-3):.0f} MHz over the collected duration)")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            b = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS
+            derived.append(f"mfma_busy_cycles_per_simd: {b:.0f} (fraction of kernel_cycles {b / cyc:.3f})")
+        if "SQ_ACTIVE_INST_VALU" in mean:
+            b = 4 * mean["SQ_ACTIVE_INST_VALU"] / SIMDS
+            derived.append(f"valu_busy_cycles_per_simd: {b:.0f} (fraction of kernel_cycles {b / cyc:.3f}; "
+                           "SQ_ACTIVE_INST_VALU is in quad-cycles)")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in mean:
+            derived.append(f"mfma_valu_coexec_fraction: {mean['SQ_VALU_MFMA_COEXEC_CYCLES'] / (cyc * SIMDS):.3f}")
+        if "SQ_WAVES" in mean and "SQ_INSTS_VALU" in mean:
+            derived.append(f"valu_instructions_per_wave: {mean['SQ_INSTS_VALU'] / mean['SQ_WAVES']:.0f}")
+        if "SQ_WAVES" in mean and "SQ_INSTS_MFMA" in mean:
+            derived.append(f"mfma_instructions_per_wave: {mean['SQ_INSTS_MFMA'] / mean['SQ_WAVES']:.0f}")
+        if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_LDS_IDX_ACTIVE" in mean:
+            c, a = mean["SQ_LDS_BANK_CONFLICT"], mean["SQ_LDS_IDX_ACTIVE"]
+            derived.append(f"lds_bank_conflict_cycles_per_access_cycle: {c / max(a - c, 1.0):.3f}")
+            derived.append(f"lds_bank_conflict_fraction_of_cu_cycles: {c / (cyc * CUS):.3f}")
+        if mops_counter and mops_counter in mean and ops:
+            done = mean[mops_counter] * 512
+            derived.append(f"mfma_ops_counted: {done:.4g} (algorithmic {ops:.4g}, ratio {done / ops:.3f})")
+        for c, unit in (("TA_TA_BUSY_sum", "ta"), ("TD_TD_BUSY_sum", "td")):
+            if c in mean:
+                derived.append(f"{unit}_busy_fraction: {mean[c] / (cyc * CUS):.3f}")
+        if "TCC_HIT_sum" in mean and "TCC_MISS_sum" in mean:
+            h, m = mean["TCC_HIT_sum"], mean["TCC_MISS_sum"]
+            derived.append(f"l2_hit_rate: {h / max(h + m, 1.0):.3f}")
+    print("\n".join(lines + ["derived:"] + ["  " + d for d in derived]))
+
+
+def summarize_trace(folder):
+    """Per-kernel durations from a kernel trace (printed to stdout): one line
+    per kernel and grid shape (a kernel that runs at several shapes gets one
+    line per shape), in order of first launch. The name is the kernel's
+    without its namespaces and argument list."""
+    groups = {}
+    for f in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+                name = name[5:] if name.startswith("void ") else name
+                if name.endswith(")"):  # drop the argument list: the "(" matching the last ")"
+                    depth, i = 0, len(name) - 1
+                    while i >= 0:
+                        depth += {")": 1, "(": -1}.get(name[i], 0)
+                        if depth == 0:
+                            break
+                        i -= 1
+                    name = name[:i]
+                name = name.replace("svdq::", "").replace("at::native::", "")
+                shape = "x".join(r[f"Grid_Size_{a}"] for a in "XYZ") + "/" + r["Workgroup_Size_X"]
+                g = groups.setdefault((name, shape), {"first": int(r["Dispatch_Id"]), "us": []})
+                g["first"] = min(g["first"], int(r["Dispatch_Id"]))
+                g["us"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if not groups:
+        raise SystemExit(f"{folder}: no kernel trace")
+    print(f"{'kernel':58s} {'grid/block':>20s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}")
+    for (name, shape), g in sorted(groups.items(), key=lambda kv: kv[1]["first"]):
+        us = g["us"]
+        print(f"{name[:58]:58s} {shape:>20s} {len(us):6d} {sum(us) / len(us):9.1f} {min(us):9.1f} {max(us):9.1f}")
 
 
 def w4a16_bytes(M, K, N):
@@ -502,6 +641,14 @@ def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, which=args.pmc_kernel)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        if len(args.summarize_counters) < 2 or args.summarize_counters[0] not in COUNTER_KERNELS:
+            raise SystemExit(f"--summarize-counters KERNEL DIR [DIR ...], KERNEL one of {', '.join(COUNTER_KERNELS)}")
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1:])
         return
     if args.gpus != 1:
         print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on one GPU only "

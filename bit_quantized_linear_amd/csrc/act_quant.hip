@@ -22,6 +22,62 @@ namespace {
 constexpr int kActWaves = 8;   // waves per block; they split the K groups
 constexpr int kActRows = 16;   // token rows per block (one 16x16 MFMA row tile)
 
+// MX shared exponent of a block: floor(log2 amax) - 2 clamped to [-127, 127],
+// -127 for amax == 0, read off the fp32 bit pattern.
+__device__ __forceinline__ int mx_exponent(float amax) {
+    const uint32_t b = __float_as_uint(amax);
+    if (b == 0u) return -127;
+    const int ex = (int)(b >> 23);
+    const int fl = ex != 0 ? ex - 127 : (31 - __clz((int)b)) - 149;  // floor(log2 amax), subnormals too
+    return min(127, max(-127, fl - 2));
+}
+
+// Eight E2M1 codes, one per nibble, with the sign of each zero code cleared:
+// the conversion keeps the sign of a negative value that rounds to zero,
+// while a zero code is +0 (a nibble's sign bit 3 survives only where its
+// magnitude bits 0-2 are not all zero).
+__device__ __forceinline__ uint32_t clear_negative_zero_fp4(uint32_t w) {
+    const uint32_t mag = w & 0x77777777u;
+    const uint32_t nonzero = (mag + 0x77777777u) & 0x88888888u;  // bit 3 of each nibble: magnitude != 0
+    return mag | (w & nonzero);
+}
+
+// 1/7 rounded to fp64, for the group scale amax / 7.
+constexpr double kRcp7 = 1.0 / 7.0;
+
+// The FP6 E2M3 value c / 8 of code c = clamp(RNE(fp32(x_hat / scale)), -7,
+// 7), with +0 for a zero code (the fma adds +0, which turns -0 into +0 and
+// leaves every other value as it is).
+__device__ __forceinline__ float fp6_value(float xh, double rscale) {
+    const float c = fminf(7.0f, fmaxf(-7.0f, rintf(quotient_fp32(xh, rscale))));
+    return __builtin_fmaf(c, 0.125f, 0.0f);
+}
+
+// FP6 E2M3 fields of v[0..15] (values that are exactly representable),
+// packed LSB-first into 3 dwords. The conversion interleaves its two
+// 16-value operands field by field (first[0], second[0], first[1], ...), so
+// even-indexed values go in the first and odd-indexed ones in the second;
+// their upper halves would fill three more dwords, which are not used.
+__device__ __forceinline__ void pack_fp6_16(const float (&v)[16], uint32_t (&w)[3]) {
+    // the upper halves are left undefined, so that no register is spent or
+    // copied for them (the compiler may overlap the two operands)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wuninitialized"
+    f32x16 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = v[2 * i];
+        b[i] = v[2 * i + 1];
+    }
+    const auto r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 1.0f);
+#pragma clang diagnostic pop
+    w[0] = r[0];
+    w[1] = r[1];
+    w[2] = r[2];
+}
+
+enum ActFmt { kInt4 = 0, kFp6 = 1, kMx = 2 };
+
 // One block owns 16 token rows and a range of K groups (all of K, or a
 // 1 / gridDim.y share when the launcher splits K across blocks so that
 // small batches still fill the chip); wave w takes the range's groups w,
@@ -33,29 +89,6 @@ constexpr int kActRows = 16;   // token rows per block (one 16x16 MFMA row tile)
 // mapping. The 8 waves' fp32 partial T tiles are summed in wave order through
 // LDS; with K split, each block stores its fp32 partial and a second kernel
 // sums the partials in K order, so T is deterministic either way.
-// E2M1 code of q (|q| < 8): nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to
-// the even mantissa (rintf rounds half to even, and in each binade the even
-// multiple of the quantum is the even mantissa), saturating at 6; bit 3 is
-// the sign; a value that rounds to zero is +0.
-__device__ __forceinline__ uint32_t e2m1_code(float q) {
-    const float m = fabsf(q);
-    const float r = m < 2.0f ? rintf(2.0f * m) * 0.5f : (m < 4.0f ? rintf(m) : fminf(6.0f, 2.0f * rintf(0.5f * m)));
-    const int c = r < 2.0f ? (int)(2.0f * r) : (r < 4.0f ? (int)r + 2 : (int)(0.5f * r) + 4);
-    return (uint32_t)c | ((c != 0 && q < 0.0f) ? 8u : 0u);
-}
-
-// MX shared exponent of a block: floor(log2 amax) - 2 clamped to [-127, 127],
-// -127 for amax == 0, read off the fp32 bit pattern.
-__device__ __forceinline__ int mx_exponent(float amax) {
-    const uint32_t b = __float_as_uint(amax);
-    if (b == 0u) return -127;
-    const int ex = (int)(b >> 23);
-    const int fl = ex != 0 ? ex - 127 : (31 - __clz((int)b)) - 149;  // floor(log2 amax), subnormals too
-    return min(127, max(-127, fl - 2));
-}
-
-enum ActFmt { kInt4 = 0, kFp6 = 1, kMx = 2 };
-
 // kFmt: kInt4 / kFp6 write INT4 codes with fp32 group scales (sx [K/64, M]);
 // kMx writes MXFP4 codes with E8M0 block scales (sx points to u8 [K/32][ld]).
 template <int kFmt, int RT>
@@ -108,21 +141,18 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
         rcp[wave][lane] = 1.0 / (double)sg;
         __builtin_amdgcn_wave_barrier();
         const double *rq = &rcp[wave][quad * 16];
-        float xb16[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t w0 = (i < 2) ? xa[2 * i] : xb[2 * (i - 2)];
-            const uint32_t w1 = (i < 2) ? xa[2 * i + 1] : xb[2 * (i - 2) + 1];
-            xb16[4 * i + 0] = bf16_bits_to_f32(w0 & 0xFFFFu);
-            xb16[4 * i + 1] = bf16_bits_to_f32(w0 >> 16);
-            xb16[4 * i + 2] = bf16_bits_to_f32(w1 & 0xFFFFu);
-            xb16[4 * i + 3] = bf16_bits_to_f32(w1 >> 16);
-        }
         // X_hat = fp32(X / s), the IEEE quotient, computed as
         // fp32(double(x) * fp64(1/s)): see quotient_fp32 for why it is exact
         float xh[16];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) xh[t] = quotient_fp32(xb16[t], rq[t]);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w0 = (i < 2) ? xa[2 * i] : xb[2 * (i - 2)];
+            const uint32_t w1 = (i < 2) ? xa[2 * i + 1] : xb[2 * (i - 2) + 1];
+            xh[4 * i + 0] = quotient_fp32(bf16_bits_to_f32(w0 & 0xFFFFu), rq[4 * i + 0]);
+            xh[4 * i + 1] = quotient_fp32(bf16_bits_to_f32(w0 >> 16), rq[4 * i + 1]);
+            xh[4 * i + 2] = quotient_fp32(bf16_bits_to_f32(w1 & 0xFFFFu), rq[4 * i + 2]);
+            xh[4 * i + 3] = quotient_fp32(bf16_bits_to_f32(w1 >> 16), rq[4 * i + 3]);
+        }
         __builtin_amdgcn_wave_barrier();
         // bamax: the 32-channel half of the group (lanes of quads 0-1 or 2-3),
         // amax: the whole group
@@ -138,8 +168,12 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f32x4 s4 = sp[i];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) xh[4 * i + t] = xb16[4 * i + t] / s4[t];
+                const uint32_t w0 = (i < 2) ? xa[2 * i] : xb[2 * (i - 2)];
+                const uint32_t w1 = (i < 2) ? xa[2 * i + 1] : xb[2 * (i - 2) + 1];
+                xh[4 * i + 0] = bf16_bits_to_f32(w0 & 0xFFFFu) / s4[0];
+                xh[4 * i + 1] = bf16_bits_to_f32(w0 >> 16) / s4[1];
+                xh[4 * i + 2] = bf16_bits_to_f32(w1 & 0xFFFFu) / s4[2];
+                xh[4 * i + 3] = bf16_bits_to_f32(w1 >> 16) / s4[3];
             }
             bamax = 0.0f;
 #pragma unroll
@@ -147,19 +181,27 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
             bamax = fmaxf(bamax, __shfl_xor(bamax, 16));
             amax = fmaxf(bamax, __shfl_xor(bamax, 32));
         }
-        const float scale = amax / 7.0f;
-        // code = RNE(fp32(x_hat / scale)), the quotient again via fp64
-        const double rscale = scale != 0.0f ? 1.0 / (double)scale : 0.0;
         if constexpr (kFmt == kMx) {
             // MXFP4: the lane's 16 channels lie in block 2g + quad / 2; its
-            // codes are x_hat / 2^e (exact, a power of two: 2^-e is a normal
-            // fp32 for every clamped e) in E2M1, 8 bytes at byte 8 (quad % 2)
-            // of the row's 16-byte half h = quad / 2 of the group
+            // codes are E2M1 of x_hat / 2^e (x_hat * 2^-e is exact: 2^-e is a
+            // normal fp32 for every clamped e, and a product that underflows
+            // is far below the smallest nonzero code). The conversion rounds
+            // to nearest, ties to the even mantissa, saturating at 6; its
+            // operands fill the low and the high nibble of the byte it
+            // writes. 8 bytes at byte 8 (quad % 2) of the row's 16-byte half
+            // h = quad / 2 of the group.
             const int e = mx_exponent(bamax);
             const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
-            uint32_t packed[2] = {0u, 0u};
+            uint32_t packed[2];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) packed[t >> 3] |= e2m1_code(xh[t] * inv) << (4 * (t & 7));
+            for (int h = 0; h < 2; ++h) {
+                uint32_t w = 0u;
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[8 * h + 0] * inv, xh[8 * h + 1] * inv, 1.0f, 0);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[8 * h + 2] * inv, xh[8 * h + 3] * inv, 1.0f, 1);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[8 * h + 4] * inv, xh[8 * h + 5] * inv, 1.0f, 2);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, xh[8 * h + 6] * inv, xh[8 * h + 7] * inv, 1.0f, 3);
+                packed[h] = clear_negative_zero_fp4(w);
+            }
             if (row_ok) {
                 const int b0 = m & ~127;
                 const int nb = min(128, M - b0);
@@ -169,59 +211,61 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
                 if ((quad & 1) == 0)
                     static_cast<uint8_t *>(sx_out)[(size_t)(2 * g + (quad >> 1)) * sx_ld + m] = (uint8_t)(e + 127);
             }
-        } else if constexpr (kFmt == kInt4) {
-            // INT4 container: two's-complement nibbles, low nibble = even k
-            uint32_t packed[2] = {0u, 0u};
-            if (scale != 0.0f) {
-#pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    const uint32_t nib = (uint32_t)int4_code(xh[t], rscale) & 0xFu;
-                    packed[t >> 3] |= nib << (4 * (t & 7));
-                }
-            }
-            if (row_ok)
-                *reinterpret_cast<u32x2 *>(qx + (size_t)m * (K / 2) + kb / 2) = u32x2{packed[0], packed[1]};
         } else {
-            // FP6 container: each code c as FP6 E2M3 of value c / 8 (sign bit,
-            // zero exponent, 3-bit magnitude), 6-bit fields packed LSB-first
-            // into the 24 bytes H_h of its half h = quad / 2; this lane's 16
-            // codes are bytes [12 (quad % 2), +12) of H_h. In the row's 48
-            // bytes of the group, H_h[0:16] sits at 16 h and H_h[16:24] at
-            // 32 + 8 h.
-            uint32_t w[3] = {0u, 0u, 0u};
-            if (scale != 0.0f) {
+            // scale = fp32(amax / 7): amax is 0 or at least 2^-100 here, so
+            // the fp64 reciprocal product is the IEEE quotient (quotient_fp32)
+            const float scale = quotient_fp32(amax, kRcp7);
+            // code = RNE(fp32(x_hat / scale)), the quotient again via fp64
+            const double rscale = scale != 0.0f ? 1.0 / (double)scale : 0.0;
+            if constexpr (kFmt == kInt4) {
+                // INT4 container: two's-complement nibbles, low nibble = even k
+                uint32_t packed[2] = {0u, 0u};
+                if (scale != 0.0f) {
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    const uint32_t v = fp6_field(int4_code(xh[t], rscale));
-                    const int bit = 6 * t;
-                    w[bit >> 5] |= v << (bit & 31);
-                    if ((bit & 31) > 26) w[(bit >> 5) + 1] |= v >> (32 - (bit & 31));
+                    for (int t = 0; t < 16; ++t) {
+                        const uint32_t nib = (uint32_t)int4_code(xh[t], rscale) & 0xFu;
+                        packed[t >> 3] |= nib << (4 * (t & 7));
+                    }
+                }
+                if (row_ok)
+                    *reinterpret_cast<u32x2 *>(qx + (size_t)m * (K / 2) + kb / 2) = u32x2{packed[0], packed[1]};
+            } else {
+                // FP6 container: each code c as FP6 E2M3 of value c / 8 (sign
+                // bit, zero exponent, 3-bit magnitude), 6-bit fields packed
+                // LSB-first into the 24 bytes H_h of its half h = quad / 2;
+                // this lane's 16 codes are bytes [12 (quad % 2), +12) of H_h.
+                // In the row's 48 bytes of the group, H_h[0:16] sits at 16 h
+                // and H_h[16:24] at 32 + 8 h.
+                float v[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) v[t] = fp6_value(xh[t], rscale);
+                uint32_t w[3];
+                pack_fp6_16(v, w);
+                if (row_ok) {
+                    // blocks of 128 rows; inside a block, group g's rows
+                    // follow one another (48 bytes each) after the block's
+                    // earlier groups
+                    const int b0 = m & ~127;
+                    const int nb = min(128, M - b0);
+                    uint8_t *grp = qx + (size_t)b0 * (K / 4 * 3) + ((size_t)g * nb + (m - b0)) * 48;
+                    const int h = quad >> 1;
+                    uint32_t *d0, *d1, *d2;
+                    if ((quad & 1) == 0) {
+                        d0 = reinterpret_cast<uint32_t *>(grp + 16 * h);
+                        d1 = d0 + 1;
+                        d2 = d0 + 2;
+                    } else {
+                        d0 = reinterpret_cast<uint32_t *>(grp + 16 * h + 12);
+                        d1 = reinterpret_cast<uint32_t *>(grp + 32 + 8 * h);
+                        d2 = d1 + 1;
+                    }
+                    *d0 = w[0];
+                    *d1 = w[1];
+                    *d2 = w[2];
                 }
             }
-            if (row_ok) {
-                // blocks of 128 rows; inside a block, group g's rows follow
-                // one another (48 bytes each) after the block's earlier groups
-                const int b0 = m & ~127;
-                const int nb = min(128, M - b0);
-                uint8_t *grp = qx + (size_t)b0 * (K / 4 * 3) + ((size_t)g * nb + (m - b0)) * 48;
-                const int h = quad >> 1;
-                uint32_t *d0, *d1, *d2;
-                if ((quad & 1) == 0) {
-                    d0 = reinterpret_cast<uint32_t *>(grp + 16 * h);
-                    d1 = d0 + 1;
-                    d2 = d0 + 2;
-                } else {
-                    d0 = reinterpret_cast<uint32_t *>(grp + 16 * h + 12);
-                    d1 = reinterpret_cast<uint32_t *>(grp + 32 + 8 * h);
-                    d2 = d1 + 1;
-                }
-                *d0 = w[0];
-                *d1 = w[1];
-                *d2 = w[2];
-            }
-        }
-        if constexpr (kFmt != kMx)
             if (row_ok && quad == 0) static_cast<float *>(sx_out)[(size_t)g * M + m] = scale;
+        }
 
         // low-rank down-projection on raw X (1/s folded into L1s)
 #pragma unroll
