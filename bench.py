@@ -548,6 +548,24 @@ def w4a4_config_line(name, steps, warmup):
             "gemm_frac_fp6_peak": round(gemm_tops / FP6_PEAK_TFLOPS, 4), "outputs_finite": finite}
 
 
+def library_int8_gemm_ms(M, K, N, steps, warmup):
+    """Time per call of the library int8 GEMM (torch._int_mm, hipBLASLt on
+    this platform) on the same shape and operand layout as the W8A8 GEMM
+    (codes [M, K] row-major times the weight codes [N, K] row-major, i.e.
+    their transpose as a view), or None where it is not available. Context
+    for the W8A8 GEMM's time, not part of any step."""
+    import torch
+
+    try:
+        g = torch.Generator(device="cuda").manual_seed(7)
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+        w = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+        ms, _, _, _ = time_steps([lambda: torch._int_mm(a, w.t())], steps, warmup)
+        return round(ms, 5)
+    except (RuntimeError, AttributeError):
+        return None
+
+
 def w8a8_config_line(name, steps, warmup):
     """The W8A8 tensorwise linear on a configuration (library preparation)."""
     import torch
@@ -572,11 +590,13 @@ def w8a8_config_line(name, steps, warmup):
 
     ms8, _, _, each = time_steps([w8], steps, warmup)
     ops8 = 2.0 * c8.M * c8.N * c8.K
-    log(f"[bench] {name}: {ms8:.4f} ms")
+    lib = library_int8_gemm_ms(c8.M, c8.K, c8.N, steps, warmup)
+    log(f"[bench] {name}: {ms8:.4f} ms (library int8 GEMM alone on the same shape: {lib} ms)")
     return {"workload": f"{name}: W8A8 tensorwise M={c8.M} K={c8.K} N={c8.N}",
             "ms": round(ms8, 5), "step_ms_median": round(float(np.median(each)), 5),
             "TOPS": round(ops8 / (ms8 * 1e-3) / 1e12, 2),
-            "pct_int8_roofline": round(100.0 * ops8 / (ms8 * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)}
+            "pct_int8_roofline": round(100.0 * ops8 / (ms8 * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
+            "library_int8_gemm_ms": lib}
 
 
 def measured_peaks():
@@ -891,10 +911,12 @@ def main():
 
         ms8, _, _, _ = time_steps([w8], args.steps, args.warmup)
         ops8 = 2.0 * c8.M * c8.N * c8.K
+        lib8 = library_int8_gemm_ms(c8.M, c8.K, c8.N, args.steps, args.warmup)
         out["w8a8"] = {"workload": f"W8A8 tensorwise M={c8.M} K={c8.K} N={c8.N}",
                        "ms": round(ms8, 5), "TOPS": round(ops8 / (ms8 * 1e-3) / 1e12, 2),
-                       "pct_int8_roofline": round(100.0 * ops8 / (ms8 * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)}
-        log(f"[bench] w8a8 {ms8:.4f} ms")
+                       "pct_int8_roofline": round(100.0 * ops8 / (ms8 * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
+                       "library_int8_gemm_ms": lib8}
+        log(f"[bench] w8a8 {ms8:.4f} ms (library int8 GEMM alone on the same shape: {lib8} ms)")
         if not args.no_cpu_baseline:
             out["w8a8"]["cpu_baseline"] = cpu_baseline_w8a8(c8, X8, W8, b8)
             log(f"[bench] w8a8 cpu baseline {out['w8a8']['cpu_baseline']['seconds']:.1f}s")
