@@ -9,6 +9,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "device_common.h"
@@ -19,8 +20,8 @@ namespace svdq {
 
 namespace {
 
-constexpr int kActWaves = 8;   // waves per block; they split the K groups
-constexpr int kActRows = 16;   // token rows per block (one 16x16 MFMA row tile)
+constexpr int kActWaves = 4;   // waves per block, one 16-row tile each
+constexpr int kActRows = 16;   // token rows per wave (one 16x16 MFMA row tile)
 
 // MX shared exponent of a block: floor(log2 amax) - 2 clamped to [-127, 127],
 // -127 for amax == 0, read off the fp32 bit pattern.
@@ -78,17 +79,23 @@ __device__ __forceinline__ void pack_fp6_16(const float (&v)[16], uint32_t (&w)[
 
 enum ActFmt { kInt4 = 0, kFp6 = 1, kMx = 2 };
 
-// One block owns 16 token rows and a range of K groups (all of K, or a
-// 1 / gridDim.y share when the launcher splits K across blocks so that
-// small batches still fill the chip); wave w takes the range's groups w,
-// w + 8, ... . Lane l holds row (l % 16) and the 16 consecutive channels
-// [64 g + 16 (l / 16), +16) of group g: two 128-bit loads of X. The four
-// lanes of a row meet through two cross-lane max steps for the group absmax.
-// For the branch, the lane's 16 channels feed two 16x16x32 bf16 MFMAs per
-// rank tile (8 channels each); B comes from l1t with the same channel
-// mapping. The 8 waves' fp32 partial T tiles are summed in wave order through
-// LDS; with K split, each block stores its fp32 partial and a second kernel
-// sums the partials in K order, so T is deterministic either way.
+// One block of 4 waves owns 64 token rows (16 per wave) and a range of K
+// groups (all of K, or a 1 / gridDim.y share when the launcher splits K
+// across blocks so that the chip fills); the waves walk the range's groups
+// in step. Lane l holds row (l % 16) of its wave's tile and the 16
+// consecutive channels [64 g + 16 (l / 16), +16) of group g: two 128-bit
+// loads of X, issued one group ahead. The four lanes of a row meet through
+// two cross-lane max steps for the group absmax. What every wave needs of a
+// group -- the L1s slice [rank][64 channels] and 1/s of the 64 channels --
+// is staged once per block in LDS (double buffered, one barrier per group):
+// the slice is loaded into registers one group ahead and written after the
+// barrier, and one wave (the waves take turns) loads the group's smoothing
+// factors and computes their fp64 reciprocals. For the branch, the lane's 16
+// channels feed two 16x16x32 bf16 MFMAs per rank tile (8 channels each),
+// with B from the staged slice in the same channel mapping; each wave keeps
+// its own rows' T, so no reduction across waves is needed. With K split,
+// each block stores its fp32 partial and a second kernel sums the partials
+// in K order, so T is deterministic either way.
 // kFmt: kInt4 / kFp6 write INT4 codes with fp32 group scales (sx [K/64, M]);
 // kMx writes MXFP4 codes with E8M0 block scales (sx points to u8 [K/32][ld]).
 template <int kFmt, int RT>
@@ -98,14 +105,18 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
     uint8_t *__restrict__ qx, void *__restrict__ sx_out, int sx_ld, uint16_t *__restrict__ T,
     float *__restrict__ tpart) {
     constexpr int kRT = RT > 0 ? RT : 1;  // rank tiles held (rank / 16, at least one array slot)
-    __shared__ float red[kActWaves][kActRows][16 * kRT];
-    __shared__ double rcp[kActWaves][SVDQ_GROUP];  // per wave: 1/s of its current group's channels
+    constexpr int kLsPitch = 2 * SVDQ_GROUP + 16;  // bytes per rank row of a staged L1s slice (padded)
+    // per group, shared by the block's waves: the L1s slice [rank][64 channels]
+    // and 1/s of the 64 channels, double buffered
+    __shared__ __attribute__((aligned(16))) uint8_t ls[2][16 * kRT * kLsPitch];
+    __shared__ double rcp[2][SVDQ_GROUP];
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int row = lane & 15;
     const int quad = lane >> 4;
-    const int m0 = blockIdx.x * kActRows;
+    const int m0 = blockIdx.x * (kActWaves * kActRows) + wave * kActRows;
     const int m = m0 + row;
     const bool row_ok = m < M;
     const int G = K / SVDQ_GROUP;
@@ -116,31 +127,57 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
 #pragma unroll
     for (int i = 0; i < kRT; ++i) tacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // X and the smoothing factor of the wave's next group are loaded one
-    // group ahead, so their latency overlaps the current group's work
-    u32x4 nxa = {0u, 0u, 0u, 0u}, nxb = {0u, 0u, 0u, 0u};
-    float ns = 1.0f;
-    auto load_next = [&](int g) {
+    // a group's L1s slice is rank rows of 128 bytes, 8 chunks of 16 bytes
+    // each; thread t loads chunks t, t + 256 (one group ahead, into
+    // registers) and writes them into the staged slice after the group's
+    // barrier. The smoothing factors of a group are loaded by one wave (the
+    // waves take turns), which also computes their reciprocals.
+    constexpr int kPer = (16 * kRT * 8 + kActWaves * 64 - 1) / (kActWaves * 64);
+    u32x4 lnext[kPer];
+    float snext = 1.0f;
+    auto ls_load = [&](int g) __attribute__((always_inline)) {
         if (g < g_hi) {
-            if (row_ok) {
-                const u32x4 *p = reinterpret_cast<const u32x4 *>(X + (size_t)m * K + g * SVDQ_GROUP + quad * 16);
-                nxa = p[0];
-                nxb = p[1];
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int c = tid + kActWaves * 64 * j;
+                if (c < rank * 8)
+                    lnext[j] = *reinterpret_cast<const u32x4 *>(l1t + (size_t)(c >> 3) * K + g * SVDQ_GROUP +
+                                                                (c & 7) * 8);
             }
-            ns = smooth[g * SVDQ_GROUP + lane];
+            if (wave == (g & (kActWaves - 1))) snext = smooth[g * SVDQ_GROUP + lane];
         }
     };
-    load_next(g_lo + wave);
-    for (int g = g_lo + wave; g < g_hi; g += kActWaves) {
+    auto ls_store = [&](int g, int b) __attribute__((always_inline)) {
+        if (g < g_hi) {
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int c = tid + kActWaves * 64 * j;
+                if (c < rank * 8) *reinterpret_cast<u32x4 *>(&ls[b][(c >> 3) * kLsPitch + (c & 7) * 16]) = lnext[j];
+            }
+            if (wave == (g & (kActWaves - 1))) rcp[b][lane] = 1.0 / (double)snext;
+        }
+    };
+
+    // X of the wave's next group is loaded one group ahead
+    u32x4 nxa = {0u, 0u, 0u, 0u}, nxb = {0u, 0u, 0u, 0u};
+    auto load_next = [&](int g) __attribute__((always_inline)) {
+        if (g < g_hi && row_ok) {
+            const u32x4 *p = reinterpret_cast<const u32x4 *>(X + (size_t)m * K + g * SVDQ_GROUP + quad * 16);
+            nxa = p[0];
+            nxb = p[1];
+        }
+    };
+    load_next(g_lo);
+    ls_load(g_lo);
+    ls_store(g_lo, 0);
+    __syncthreads();
+    int buf = 0;
+    for (int g = g_lo; g < g_hi; ++g, buf ^= 1) {
         const int kb = g * SVDQ_GROUP + quad * 16;
         const u32x4 xa = nxa, xb = nxb;
-        const float sg = ns;
-        load_next(g + kActWaves);
-        // 1/s of the group's 64 channels, one fp64 division per lane, shared
-        // through this wave's slice of LDS
-        rcp[wave][lane] = 1.0 / (double)sg;
-        __builtin_amdgcn_wave_barrier();
-        const double *rq = &rcp[wave][quad * 16];
+        load_next(g + 1);
+        ls_load(g + 1);
+        const double *rq = &rcp[buf][quad * 16];
         // X_hat = fp32(X / s), the IEEE quotient, computed as
         // fp32(double(x) * fp64(1/s)): see quotient_fp32 for why it is exact
         float xh[16];
@@ -153,7 +190,6 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
             xh[4 * i + 2] = quotient_fp32(bf16_bits_to_f32(w1 & 0xFFFFu), rq[4 * i + 2]);
             xh[4 * i + 3] = quotient_fp32(bf16_bits_to_f32(w1 >> 16), rq[4 * i + 3]);
         }
-        __builtin_amdgcn_wave_barrier();
         // bamax: the 32-channel half of the group (lanes of quads 0-1 or 2-3),
         // amax: the whole group
         float bamax = 0.0f;
@@ -267,7 +303,8 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
             if (row_ok && quad == 0) static_cast<float *>(sx_out)[(size_t)g * M + m] = scale;
         }
 
-        // low-rank down-projection on raw X (1/s folded into L1s)
+        // low-rank down-projection on raw X (1/s folded into L1s); B from
+        // the staged slice, same channel mapping as the lane's X
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const bf16x8 a = __builtin_bit_cast(bf16x8, s == 0 ? xa : xb);
@@ -275,36 +312,34 @@ __global__ __launch_bounds__(kActWaves * 64) void quantize_act_kernel(
             for (int rt = 0; rt < kRT; ++rt) {
                 if (rt < rtiles) {
                     const bf16x8 b = *reinterpret_cast<const bf16x8 *>(
-                        l1t + (size_t)(rt * 16 + row) * K + kb + 8 * s);
+                        &ls[buf][(rt * 16 + row) * kLsPitch + (quad * 16 + 8 * s) * 2]);
                     tacc[rt] = mfma_bf16_16x16x32(a, b, tacc[rt]);
                 }
             }
         }
+        // the next group's slice and 1/s into the other buffer (read by no
+        // one since the barrier that ended the previous group); the barrier
+        // makes them visible and ends this group's reads of `buf`
+        ls_store(g + 1, buf ^ 1);
+        __syncthreads();
     }
 
     if (rtiles == 0) return;
     // 16x16 output: lane holds column (lane % 16) = rank index within the
-    // tile, rows 4 (lane / 16) + t
+    // tile, rows 4 (lane / 16) + t of the wave's 16 rows
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
         if (rt < rtiles) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) red[wave][4 * quad + t][rt * 16 + row] = tacc[rt][t];
-        }
-    }
-    __syncthreads();
-    const int elems = kActRows * rank;
-    for (int e = threadIdx.x; e < elems; e += blockDim.x) {
-        const int r = e / rank;
-        const int j = e - r * rank;
-        float v = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kActWaves; ++w) v += red[w][r][j];
-        if (m0 + r < M) {
-            if (gridDim.y == 1)
-                T[(size_t)(m0 + r) * rank + j] = (uint16_t)f32_to_bf16_bits(v);
-            else
-                tpart[((size_t)blockIdx.y * M + m0 + r) * rank + j] = v;
+            for (int t = 0; t < 4; ++t) {
+                const int mm = m0 + 4 * quad + t;
+                if (mm < M) {
+                    if (gridDim.y == 1)
+                        T[(size_t)mm * rank + rt * 16 + row] = (uint16_t)f32_to_bf16_bits(tacc[rt][t]);
+                    else
+                        tpart[((size_t)blockIdx.y * M + mm) * rank + rt * 16 + row] = tacc[rt][t];
+                }
+            }
         }
     }
 }
@@ -363,21 +398,21 @@ static void launch_act_rt(dim3 grid, hipStream_t stream, int fmt, const uint16_t
                            l1t, M, K, rank, qx, sx, sx_ld, T, tpart);
 }
 
-// How many blocks share the K range of one 16-row tile: the largest divisor
-// d of the group count that leaves every wave whole groups (G / d a multiple
-// of 8, the waves per block) and keeps the grid within 4 blocks per compute
-// unit, or within 8 when each block still has 4 groups per wave. More parts
-// balance the grid better but add T partials to write and sum (measured at
-// M = 4608: 3 parts best at K = 3072, 6 at K = 12288).
+// How many blocks share the K range of one 64-row block (K parts): enough
+// to give the GPU about 2048 blocks of four waves, but no fewer than six
+// groups per block (each group costs the block a barrier and a staged L1s
+// slice, and each part a [M][rank] fp32 slice of partial sums), and at most
+// 131072 / M parts, so that the partials of every accepted shape (rank <=
+// 64) fit the 32 MiB scratch of the allocation-free pass. Measured at
+// M = 4608: 8 parts best at K = 3072 (6 groups each), 24-32 at K = 12288;
+// at M = 32760, K = 5120: 2-4 parts.
 int act_k_parts(int M, int K) {
-    const int64_t blocks = (M + kActRows - 1) / kActRows;
+    if (M <= 0) return 1;
+    const int64_t row_blocks = (M + kActWaves * kActRows - 1) / (kActWaves * kActRows);
     const int G = K / SVDQ_GROUP;
-    int kp = 1;
-    for (int d = 2; d <= G / kActWaves; ++d) {
-        if (G % d != 0 || (G / d) % kActWaves != 0) continue;
-        if (blocks * d <= 1024 || (blocks * d <= 2048 && G / d >= 4 * kActWaves)) kp = d;
-    }
-    return kp;
+    int64_t kp = std::min<int64_t>(G / 6, 2048 / row_blocks);
+    kp = std::min<int64_t>(kp, 131072 / M);
+    return (int)std::max<int64_t>(1, kp);
 }
 
 size_t act_workspace_size(int M, int K, int rank) {
@@ -393,7 +428,7 @@ static hipError_t launch_act(const uint16_t *X, const float *smooth, const uint1
                       hipStream_t stream) {
     const int kp = (rank == 0 || workspace) ? act_k_parts(M, K) : 1;
     float *tpart = kp > 1 && rank ? workspace : nullptr;
-    const dim3 grid((M + kActRows - 1) / kActRows, kp);
+    const dim3 grid((M + kActWaves * kActRows - 1) / (kActWaves * kActRows), kp);
     switch (rank / 16) {  // rank % 16 == 0 and rank <= 64 are checked by the caller
         case 0: launch_act_rt<0>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T, tpart); break;
         case 1: launch_act_rt<1>(grid, stream, fmt, X, smooth, l1t, M, K, rank, qx, sx, sx_ld, T, tpart); break;
@@ -408,11 +443,10 @@ static hipError_t launch_act(const uint16_t *X, const float *smooth, const uint1
 
 // Scratch of the allocation-free activation pass (svdq_quantize_act_noalloc):
 // the fp32 partial sums of T, [parts][M][rank], when K is split across
-// blocks. act_k_parts keeps parts x ceil(M / 16) <= 2048 blocks whenever it
-// splits, so parts x M <= 32768 and the partials never exceed 32768 x 64 x 4
-// bytes = 8 MiB. Every element the reduction reads is written by the same
-// call first, so nothing needs clearing; calls that overlap on one device
-// share this array and race.
+// blocks. act_k_parts keeps parts x M <= 131072, so the partials never exceed
+// 131072 x 64 x 4 bytes = 32 MiB. Every element the reduction reads is
+// written by the same call first, so nothing needs clearing; calls that
+// overlap on one device share this array and race.
 static __device__ __align__(256) float scratch[kActScratchBytes / sizeof(float)];
 
 namespace {

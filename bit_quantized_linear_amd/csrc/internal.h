@@ -43,7 +43,7 @@ size_t act_workspace_size(int M, int K, int rank);
 // fixed device scratch of svdq_quantize_act_noalloc (bytes; covers
 // act_workspace_size for every supported shape) and its address on the
 // current device, looked up once per device
-constexpr size_t kActScratchBytes = (size_t)8 << 20;
+constexpr size_t kActScratchBytes = (size_t)32 << 20;
 hipError_t act_scratch_pointer(float **out);
 hipError_t launch_quantize_act(const uint16_t *X, const float *smooth,
                                const uint16_t *l1t, int M, int K, int rank,

@@ -301,10 +301,10 @@ svdq_status svdq_quantize_act(const uint16_t *X, const float *smooth,
  * capture, tight serving loops, harnesses that forbid allocation. Same
  * arguments, results and errors as svdq_quantize_act given a workspace (the
  * same kernels and the same split of K, so the outputs are identical); the
- * fp32 partial sums of T go to a fixed 8 MiB device array inside the
+ * fp32 partial sums of T go to a fixed 32 MiB device array inside the
  * library (one per device, held until the process ends; its address is
  * looked up on the first call on each device). Every shape the pass accepts
- * fits it (when K is split in p parts, p * M <= 32768 and rank <= 64); a
+ * fits it (when K is split in p parts, p * M <= 131072 and rank <= 64); a
  * call that would need more is refused with SVDQ_ERR_UNSUPPORTED_SHAPE
  * before any launch. The array is shared by every call on a device: calls
  * that overlap in time on one device (different streams, threads or
