@@ -43,40 +43,6 @@ __device__ __forceinline__ uint32_t clear_negative_zero_fp4(uint32_t w) {
     return mag | (w & nonzero);
 }
 
-// 1/7 rounded to fp64, for the group scale amax / 7.
-constexpr double kRcp7 = 1.0 / 7.0;
-
-// The FP6 E2M3 value c / 8 of code c = clamp(RNE(fp32(x_hat / scale)), -7,
-// 7), with +0 for a zero code (the fma adds +0, which turns -0 into +0 and
-// leaves every other value as it is).
-__device__ __forceinline__ float fp6_value(float xh, double rscale) {
-    const float c = fminf(7.0f, fmaxf(-7.0f, rintf(quotient_fp32(xh, rscale))));
-    return __builtin_fmaf(c, 0.125f, 0.0f);
-}
-
-// FP6 E2M3 fields of v[0..15] (values that are exactly representable),
-// packed LSB-first into 3 dwords. The conversion interleaves its two
-// 16-value operands field by field (first[0], second[0], first[1], ...), so
-// even-indexed values go in the first and odd-indexed ones in the second;
-// their upper halves would fill three more dwords, which are not used.
-__device__ __forceinline__ void pack_fp6_16(const float (&v)[16], uint32_t (&w)[3]) {
-    // the upper halves are left undefined, so that no register is spent or
-    // copied for them (the compiler may overlap the two operands)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Wuninitialized"
-    f32x16 a, b;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        a[i] = v[2 * i];
-        b[i] = v[2 * i + 1];
-    }
-    const auto r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 1.0f);
-#pragma clang diagnostic pop
-    w[0] = r[0];
-    w[1] = r[1];
-    w[2] = r[2];
-}
-
 enum ActFmt { kInt4 = 0, kFp6 = 1, kMx = 2 };
 
 // One block of 4 waves owns 64 token rows (16 per wave) and a range of K

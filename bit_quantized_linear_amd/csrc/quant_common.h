@@ -1,12 +1,15 @@
 // Device helpers shared by the activation quantizers (the standalone pass in
 // act_quant.hip and the fused MLP epilogue of the FP6 GEMM): exact fp32
-// quotients without per-element divisions, and the FP6 E2M3 field of an
-// INT4 code.
+// quotients without per-element divisions, the FP6 E2M3 field of an INT4
+// code, and the packing of codes into FP6 fields by the conversion
+// instruction.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+
+#include "device_common.h"
 
 namespace svdq {
 
@@ -40,6 +43,40 @@ __device__ __forceinline__ int int4_code(float xh, double rscale) {
 // exponent, magnitude in the 3 mantissa bits.
 __device__ __forceinline__ uint32_t fp6_field(int c) {
     return (c < 0 ? 0x20u : 0u) | (uint32_t)(c < 0 ? -c : c);
+}
+
+// 1/7 rounded to fp64, for the group scale amax / 7.
+constexpr double kRcp7 = 1.0 / 7.0;
+
+// The FP6 E2M3 value c / 8 of code c = clamp(RNE(fp32(x_hat / scale)), -7,
+// 7), with +0 for a zero code (the fma adds +0, which turns -0 into +0 and
+// leaves every other value as it is).
+__device__ __forceinline__ float fp6_value(float xh, double rscale) {
+    const float c = fminf(7.0f, fmaxf(-7.0f, rintf(quotient_fp32(xh, rscale))));
+    return __builtin_fmaf(c, 0.125f, 0.0f);
+}
+
+// FP6 E2M3 fields of v[0..15] (values that are exactly representable),
+// packed LSB-first into 3 dwords. The conversion interleaves its two
+// 16-value operands field by field (first[0], second[0], first[1], ...), so
+// even-indexed values go in the first and odd-indexed ones in the second;
+// their upper halves would fill three more dwords, which are not used.
+__device__ __forceinline__ void pack_fp6_16(const float (&v)[16], uint32_t (&w)[3]) {
+    // the upper halves are left undefined, so that no register is spent or
+    // copied for them (the compiler may overlap the two operands)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wuninitialized"
+    f32x16 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = v[2 * i];
+        b[i] = v[2 * i + 1];
+    }
+    const auto r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 1.0f);
+#pragma clang diagnostic pop
+    w[0] = r[0];
+    w[1] = r[1];
+    w[2] = r[2];
 }
 
 }  // namespace svdq

@@ -222,28 +222,34 @@ __device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t 
             }
             amax = fmaxf(amax, __shfl_xor(amax, 1));
         }
-        const float scale = amax / 7.0f;
+        // fp32(amax / 7): amax is 0 or at least 2^-100 unless the group is
+        // tiny, where the IEEE division is kept
+        const float scale = tiny ? amax / 7.0f : quotient_fp32(amax, kRcp7);
         const double rscale = scale != 0.0f ? 1.0 / (double)scale : 0.0;
-        // 32 six-bit fields, LSB first: chunk c fills bits [48 c, 48 c + 48)
+        // 32 six-bit fields, LSB first, 16 codes (two chunks) per packing
+        // conversion: codes 16 hh .. 16 hh + 15 fill fw[3 hh .. 3 hh + 2]
         uint32_t fw[6] = {0u, 0u, 0u, 0u, 0u, 0u};
         if (scale != 0.0f) {
-#pragma unroll 1
-            for (int c = 0; c < 4; ++c) {
-                float gv[8];
-                chunk(c, gv);
-                uint64_t bits48 = 0;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float xh = tiny ? gv[i] / sv[32 * qd + 8 * c + i]
-                                          : quotient_fp32(gv[i], rcp[32 * qd + 8 * c + i]);
-                    bits48 |= (uint64_t)fp6_field(int4_code(xh, rscale)) << (6 * i);
+            for (int hh = 0; hh < 2; ++hh) {
+                float v[16];
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int c = 2 * hh + cc;
+                    float gv[8];
+                    chunk(c, gv);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float xh = tiny ? gv[i] / sv[32 * qd + 8 * c + i]
+                                              : quotient_fp32(gv[i], rcp[32 * qd + 8 * c + i]);
+                        v[8 * cc + i] = fp6_value(xh, rscale);
+                    }
                 }
-                // 48 bits at bit 48 c: chunks 0, 2 start on a word, 1, 3 at bit 16
-                const uint32_t lo = (uint32_t)bits48, hi = (uint32_t)(bits48 >> 32);
-                if (c == 0) { fw[0] = lo; fw[1] = hi; }
-                else if (c == 1) { fw[1] |= lo << 16; fw[2] = (lo >> 16) | (hi << 16); }
-                else if (c == 2) { fw[3] = lo; fw[4] = hi; }
-                else { fw[4] |= lo << 16; fw[5] = (lo >> 16) | (hi << 16); }
+                uint32_t w3[3];
+                pack_fp6_16(v, w3);
+                fw[3 * hh] = w3[0];
+                fw[3 * hh + 1] = w3[1];
+                fw[3 * hh + 2] = w3[2];
             }
         }
         if (grp_ok && m < M) {
