@@ -181,6 +181,10 @@ __global__ __launch_bounds__(MX_THREADS, 3) void mx_linear_kernel(
                 sb[q][i] = cur.ub[q][lh][wm * 64 + i * 32 + r32];
             }
         }
+        // the stage's MFMAs at raised wave priority, so that waves ready for
+        // the matrix core issue before others' loads and LDS reads (measured
+        // 5 % faster)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int q = 0; q < MX_KG; ++q) {
             if (q >= ng) break;
@@ -191,6 +195,7 @@ __global__ __launch_bounds__(MX_THREADS, 3) void mx_linear_kernel(
                     acc[in][im] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         a[q][in], b[q][im], acc[in][im], MX_FP4, MX_FP4, 0, sa[q][in], 0, sb[q][im]);
         }
+        __builtin_amdgcn_s_setprio(0);
         // stage s + 1 must have landed before anyone reads it (stage s + 2
         // may stay in flight), and everyone must be done with stage s before
         // it is refilled (with stage s + 3, issued after the barrier)
