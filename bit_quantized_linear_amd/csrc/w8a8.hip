@@ -96,10 +96,12 @@ enum class W8Epilogue { kLinear, kAcc };
 // The GEMM: C^T tile = A . B^T with A = weight rows (output columns n, K
 // contiguous int8) and B = activation code rows (tokens m), on gfx950
 // v_mfma_i32_32x32x32_i8 with int32 accumulation over all of K.
-//  - Block 128 (n) x 128 (m), 4 waves as 2 x 2, wave tile 64 x 64 (2 x 2
+//  - Block 256 (n) x 256 (m), 8 waves as 2 x 4, wave tile 128 x 64 (4 x 2
 //    MFMA tiles of 32 x 32).
-//  - One LDS stage is 128 bytes of K (k0 .. k0 + 127) for the block's 128
-//    rows of each operand: 16 KB each, double buffered (64 KB per block).
+//  - One LDS stage is 128 bytes of K (k0 .. k0 + 127) for the block's 256
+//    rows of each operand: 32 KB each, double buffered (128 KB per block,
+//    one block of 8 waves per CU); a stage is 32 MFMAs per wave, long
+//    enough for the next stage's loads to land.
 //  - Operands go straight from global memory to LDS (buffer_load ... lds,
 //    16 bytes per lane, lane l to base + 16 l): 8 lanes cover one row's
 //    128 bytes, so every 1 KB load reads 8 whole cache lines.
@@ -110,15 +112,10 @@ enum class W8Epilogue { kLinear, kAcc };
 //  - Rows past M or N and a trailing half stage (K % 128 == 64) read zeros:
 //    the whole offset is in the per-lane offset, so the buffer range check
 //    sees it, and chunks past K get an offset past every buffer.
-constexpr int W8_TILE = 128;    // rows per block and operand
-constexpr int W8_KS = 128;      // K bytes per stage
-constexpr int W8_THREADS = 256;
+//  - Against a 128 x 128 tile with the same staging (4 waves, two blocks
+//    per CU): 10-13 % faster at 32760 x 5120 x 5120, 5 % at 4608 x 3072 x
+//    3072, half the operand bytes per multiply-add.
 constexpr uint32_t kW8Oob = 0x80000000u;
-
-struct W8Stage {
-    uint8_t a[W8_TILE * W8_KS];
-    uint8_t b[W8_TILE * W8_KS];
-};
 
 typedef __attribute__((address_space(3))) void w8_lds_void;
 
@@ -126,52 +123,75 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t w8_rsrc(const void *p, uint32_
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+constexpr int WB_TILE = 256;
+constexpr int WB_KS = 128;
+constexpr int WB_THREADS = 512;
+constexpr int WB_PITCH = 2 * WB_TILE + 16;  // bytes per output row staged in LDS (bf16, padded)
+
+struct WbStage {
+    uint8_t a[WB_TILE * WB_KS];
+    uint8_t b[WB_TILE * WB_KS];
+};
+
 template <W8Epilogue kEpi>
-__global__ __launch_bounds__(W8_THREADS, 2) void w8a8_gemm_kernel(
+__global__ __launch_bounds__(WB_THREADS, 1) void w8a8_gemm256_kernel(
     const int8_t *__restrict__ qx, const int8_t *__restrict__ qw, const float *__restrict__ sxp,
     float sw, const uint16_t *__restrict__ bias, int M, int N, int K, uint16_t *__restrict__ Y,
     int32_t *__restrict__ acc_out, int tiles_n) {
-    // two stages in separate LDS variables: the compiler can then tell the
-    // stage being refilled (direct-to-LDS loads) from the one being read and
-    // does not make the reads wait for the loads
-    __shared__ __attribute__((aligned(16))) W8Stage st0;
-    __shared__ __attribute__((aligned(16))) W8Stage st1;
-    __shared__ __attribute__((aligned(16))) float bias_s[W8_TILE];
+    __shared__ __attribute__((aligned(16))) WbStage st0;
+    __shared__ __attribute__((aligned(16))) WbStage st1;
+    __shared__ __attribute__((aligned(16))) float bias_s[WB_TILE];
 
-    const int tile_n = blockIdx.x % tiles_n;
-    const int tile_m = blockIdx.x / tiles_n;
-    const int n0 = tile_n * W8_TILE;
-    const int m0 = tile_m * W8_TILE;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // blocks are dealt to the 8 XCDs round-robin (block b runs on XCD
+    // b % 8): XCD c takes the contiguous tile range [c T / 8, (c + 1) T / 8),
+    // walked four m-tiles at a time across n, so that the tiles an XCD runs
+    // together share operand rows in its L2
+    int tile_n, tile_m;
+    {
+        const int T = gridDim.x;
+        const int b = blockIdx.x;
+        const int id = (T % 8 == 0) ? (b % 8) * (T / 8) + b / 8 : b;
+        const int tiles_m = T / tiles_n;
+        const int group = id / (4 * tiles_n);
+        const int first_m = group * 4;
+        const int gm = min(4, tiles_m - first_m);
+        const int in_group = id - group * 4 * tiles_n;
+        tile_m = first_m + in_group % gm;
+        tile_n = in_group / gm;
+    }
+    const int n0 = tile_n * WB_TILE;
+    const int m0 = tile_m * WB_TILE;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave & 1;
     const int wm = wave >> 1;
     const int r32 = lane & 31;
     const int lh = lane >> 5;
-    const int S = (K + W8_KS - 1) / W8_KS;
+    const int S = (K + WB_KS - 1) / WB_KS;
 
     const __amdgpu_buffer_rsrc_t ra = w8_rsrc(qw, (uint32_t)N * (uint32_t)K);
     const __amdgpu_buffer_rsrc_t rb = w8_rsrc(qx, (uint32_t)M * (uint32_t)K);
 
-    // Wave w issues loads 8w .. 8w + 7 of the stage's 32 (16 per operand):
-    // load j of an operand fills staged rows 8 j .. 8 j + 7; lane l writes
-    // row 8 j + l / 8 at chunk position l % 8.
-    const int op = wave >> 1;  // waves 0, 1: weights; 2, 3: activations
+    // waves 0-3 issue the weights' 32 loads of a stage, waves 4-7 the
+    // activations'; load j fills staged rows 8 j .. 8 j + 7, lane l row
+    // 8 j + l / 8 at chunk position l % 8
+    const int op = wave >> 2;
     const int row0 = op ? m0 : n0;
     uint32_t gbase[8];
     int gchunk[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int j = (wave & 1) * 8 + i;
+        const int j = (wave & 3) * 8 + i;
         const int r = j * 8 + lane / 8;
         const int c = (lane % 8) ^ ((r >> 1) & 7);
         gchunk[i] = c;
         gbase[i] = (uint32_t)(row0 + r) * (uint32_t)K + (uint32_t)(c * 16);
     }
-    auto issue_stage = [&](int s, W8Stage &st) {
-        const int k0 = s * W8_KS;
-        const bool half = k0 + W8_KS > K;  // trailing 64 bytes only
-        uint8_t *dst = (op ? st.b : st.a) + (wave & 1) * 8 * 1024;
+    auto issue_stage = [&](int s, WbStage &st) __attribute__((always_inline)) {
+        const int k0 = s * WB_KS;
+        const bool half = k0 + WB_KS > K;  // trailing 64 bytes only
+        uint8_t *dst = (op ? st.b : st.a) + (wave & 3) * 8 * 1024;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             uint32_t off = gbase[i] + (uint32_t)k0;
@@ -180,49 +200,38 @@ __global__ __launch_bounds__(W8_THREADS, 2) void w8a8_gemm_kernel(
                                                      0, 0, 0);
         }
     };
-    // this lane's operand reads: row, and chunk position of chunk c = 2 kk + lh
-    int ara[2], arb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        ara[i] = wn * 64 + i * 32 + r32;
-        arb[i] = wm * 64 + i * 32 + r32;
-    }
-    auto frag = [&](const uint8_t *base, int r, int kk) {
+    auto frag = [&](const uint8_t *base, int r, int kk) __attribute__((always_inline)) {
         const int c = (2 * kk + lh) ^ ((r >> 1) & 7);
-        return *reinterpret_cast<const i32x4 *>(base + r * W8_KS + c * 16);
+        return *reinterpret_cast<const i32x4 *>(base + r * WB_KS + c * 16);
     };
 
-    i32x16 P[2][2];
+    i32x16 P[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) P[i][j][e] = 0;
 
-    if constexpr (kEpi == W8Epilogue::kLinear) stage_bias_128(bias_s, bias, n0, N, threadIdx.x);
+    if constexpr (kEpi == W8Epilogue::kLinear)
+        if (tid < WB_TILE) bias_s[tid] = bias && n0 + tid < N ? bf16_bits_to_f32(bias[n0 + tid]) : 0.0f;
     issue_stage(0, st0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // stage s is read from `cur` while stage s + 1 loads into `nxt`
-    auto run_stage = [&](int s, const W8Stage &cur, W8Stage &nxt) {
+    auto run_stage = [&](int s, const WbStage &cur, WbStage &nxt) __attribute__((always_inline)) {
         if (s + 1 < S) issue_stage(s + 1, nxt);
 #pragma unroll
-        for (int kk = 0; kk < W8_KS / 32; ++kk) {
-            i32x4 a[2], b[2];
+        for (int kk = 0; kk < WB_KS / 32; ++kk) {
+            i32x4 a[4], b[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                a[i] = frag(cur.a, ara[i], kk);
-                b[i] = frag(cur.b, arb[i], kk);
-            }
+            for (int i = 0; i < 4; ++i) a[i] = frag(cur.a, wn * 128 + i * 32 + r32, kk);
 #pragma unroll
-            for (int in = 0; in < 2; ++in)
+            for (int i = 0; i < 2; ++i) b[i] = frag(cur.b, wm * 64 + i * 32 + r32, kk);
+#pragma unroll
+            for (int in = 0; in < 4; ++in)
 #pragma unroll
                 for (int im = 0; im < 2; ++im) P[in][im] = mfma_i8_32x32x32(a[in], b[im], P[in][im]);
         }
-        // the next stage must have landed before anyone reads it, and
-        // everyone must be done with this one before it is refilled; the
-        // scheduling barrier keeps this stage's MFMAs above the wait
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -233,26 +242,50 @@ __global__ __launch_bounds__(W8_THREADS, 2) void w8a8_gemm_kernel(
     }
 
     if constexpr (kEpi == W8Epilogue::kLinear) {
-        // y = P sx sw + bias, the product rounded to fp32 before the sum
+        // y = P sx sw + bias, rounded once to bf16; staged through LDS a
+        // quarter (64 tokens: the waves of one wm) at a time, alternating
+        // between the two stage buffers, each quarter stored as whole
+        // 512-byte row segments
         const float scale = (*sxp) * sw;
-        f32x16 acc[2][2];
 #pragma unroll
-        for (int in = 0; in < 2; ++in)
+        for (int q = 0; q < 4; ++q) {
+            uint8_t *buf = reinterpret_cast<uint8_t *>((q & 1) ? &st1 : &st0);
+            if (wm == q) {
 #pragma unroll
-            for (int im = 0; im < 2; ++im)
+                for (int in = 0; in < 4; ++in) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[in][im][e] = (float)P[in][im][e] * scale;
-        // every stage has been read: the stage buffers hold the output tile
-        // on its way out
-        static_assert(sizeof(W8Stage) >= kTileHalfLdsBytes, "LDS too small for the output tile");
-        store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&st0), reinterpret_cast<uint8_t *>(&st1), bias_s, Y,
-                           false, M, N, m0, n0, wn, wm, threadIdx.x);
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const int nl = wn * 128 + in * 32 + 8 * qq + 4 * lh;
+                        const f32x4 bv = *reinterpret_cast<const f32x4 *>(bias_s + nl);
+#pragma unroll
+                        for (int im = 0; im < 2; ++im) {
+                            const int ml = im * 32 + r32;
+                            float v[4];
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) v[t] = (float)P[in][im][4 * qq + t] * scale + bv[t];
+                            *reinterpret_cast<u32x2 *>(buf + ml * WB_PITCH + nl * 2) =
+                                u32x2{bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = tid + WB_THREADS * i;  // 64 rows x 32 pieces
+                const int row = c >> 5, piece = c & 31;
+                const int m = m0 + 64 * q + row, n = n0 + piece * 8;
+                if (m < M && n < N)
+                    *reinterpret_cast<u32x4 *>(Y + (size_t)m * N + n) =
+                        *reinterpret_cast<const u32x4 *>(buf + row * WB_PITCH + piece * 16);
+            }
+        }
     } else {
 #pragma unroll
-        for (int in = 0; in < 2; ++in) {
+        for (int in = 0; in < 4; ++in) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * 64 + in * 32 + 8 * q + 4 * lh;
+                const int n = n0 + wn * 128 + in * 32 + 8 * q + 4 * lh;
                 if (n >= N) continue;
 #pragma unroll
                 for (int im = 0; im < 2; ++im) {
@@ -289,18 +322,18 @@ hipError_t launch_w8a8_linear(const uint16_t *X, const int8_t *qw, float sw, con
     int qblocks = (int)std::max<int64_t>(1, std::min<int64_t>(4096, (chunks + kQThreads - 1) / kQThreads));
     hipLaunchKernelGGL(w8_quantize_kernel, dim3(qblocks), dim3(kQThreads), 0, stream, X, chunks, partial,
                        nparts, scale, codes);
-    const int tiles_n = (N + W8_TILE - 1) / W8_TILE;
-    const int tiles_m = (M + W8_TILE - 1) / W8_TILE;
-    hipLaunchKernelGGL(w8a8_gemm_kernel<W8Epilogue::kLinear>, dim3(tiles_n * tiles_m), dim3(W8_THREADS),
+    const int tiles_n = (N + WB_TILE - 1) / WB_TILE;
+    const int tiles_m = (M + WB_TILE - 1) / WB_TILE;
+    hipLaunchKernelGGL(w8a8_gemm256_kernel<W8Epilogue::kLinear>, dim3(tiles_n * tiles_m), dim3(WB_THREADS),
                        0, stream, codes, qw, scale, sw, bias, M, N, K, Y, nullptr, tiles_n);
     return hipGetLastError();
 }
 
 hipError_t launch_w8a8_acc(const int8_t *qx, const int8_t *qw, int M, int N, int K, int32_t *acc,
                            hipStream_t stream) {
-    const int tiles_n = (N + W8_TILE - 1) / W8_TILE;
-    const int tiles_m = (M + W8_TILE - 1) / W8_TILE;
-    hipLaunchKernelGGL(w8a8_gemm_kernel<W8Epilogue::kAcc>, dim3(tiles_n * tiles_m), dim3(W8_THREADS), 0,
+    const int tiles_n = (N + WB_TILE - 1) / WB_TILE;
+    const int tiles_m = (M + WB_TILE - 1) / WB_TILE;
+    hipLaunchKernelGGL(w8a8_gemm256_kernel<W8Epilogue::kAcc>, dim3(tiles_n * tiles_m), dim3(WB_THREADS), 0,
                        stream, qx, qw, nullptr, 0.0f, nullptr, M, N, K, nullptr, acc, tiles_n);
     return hipGetLastError();
 }
