@@ -183,14 +183,15 @@ COUNTER_KERNELS = {
             "svdq_quantize_act (FP6 container), mlp_up M=4608 K=3072 rank=32", None, None),
     "mx_gemm": (MX_KERNEL_KEY, MX_SOURCES, "svdq_mx_linear (MXFP4), mlp_up M=4608 K=3072 N=12288 rank=32",
                 2 * 4608 * 3072 * 12288, "SQ_INSTS_VALU_MFMA_MOPS_F6F4"),
-    "w8a8_gemm": ("w8a8_gemm_kernel", ("w8a8.hip", "gemm_int.h", "device_common.h", "quant_common.h"),
+    "w8a8_gemm": ("w8a8_gemm256_kernel", ("w8a8.hip", "gemm_int.h", "device_common.h", "quant_common.h"),
                   "w8a8_linear GEMM, attention projection M=4608 K=3072 N=3072",
                   2 * 4608 * 3072 * 3072, "SQ_INSTS_VALU_MFMA_MOPS_I8"),
 }
 # grid sizes (work-items) of the workloads above where the kernel also runs
 # at other shapes in the same bench run: the up-projection's 36 x 96 blocks of
-# 256 threads; the activation pass's 288 row tiles x 3 K parts of 512 threads
-COUNTER_GRIDS = {"fp6_gemm": 36 * 96 * 256, "act": 288 * 3 * 512}
+# 256 threads; the activation pass's 72 blocks of 64 rows x 8 K parts of 256
+# threads
+COUNTER_GRIDS = {"fp6_gemm": 36 * 96 * 256, "act": 72 * 8 * 256}
 XCDS, CUS, SIMDS = 8, 256, 1024  # MI355X
 
 
