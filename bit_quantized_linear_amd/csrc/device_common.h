@@ -189,4 +189,78 @@ __device__ __forceinline__ void store_tile_128x128(const f32x16 (&acc)[2][2], ui
     }
 }
 
+// The same for a 128 (features) x 64 (tokens) tile whose waves (wn, wm)
+// hold features wn * 64 .. wn * 64 + 63 of tokens wm * 32 .. wm * 32 + 31
+// (one 32-token slice each): a bf16 tile goes through LDS whole (64 rows),
+// an fp32 tile in two passes of 32 tokens (the waves of one wm write,
+// everyone stores). lds needs kTile64LdsBytes bytes, 16-byte aligned and
+// not in use by anyone; the rest as for store_tile_128x128.
+constexpr int kTile64LdsBytes = 64 * kTileBf16Pitch > 32 * kTileF32Pitch ? 64 * kTileBf16Pitch
+                                                                           : 32 * kTileF32Pitch;
+
+__device__ __forceinline__ void store_tile_128x64(const f32x16 (&acc)[2][1], uint8_t *lds, const float *bias_s,
+                                                  void *__restrict__ Y, bool y_f32, int M, int N, int m0, int n0,
+                                                  int wn, int wm, int tid) {
+    const int lane = tid & 63, r32 = lane & 31, lh = lane >> 5;
+    if (!y_f32) {
+#pragma unroll
+        for (int in = 0; in < 2; ++in) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int nl = wn * 64 + in * 32 + 8 * qq + 4 * lh;
+                const f32x4 bv = *reinterpret_cast<const f32x4 *>(bias_s + nl);
+                const int ml = wm * 32 + r32;
+                float v[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = acc[in][0][4 * qq + t] + bv[t];
+                *reinterpret_cast<u32x2 *>(lds + ml * kTileBf16Pitch + nl * 2) =
+                    u32x2{bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
+            }
+        }
+        __syncthreads();
+        uint16_t *y = static_cast<uint16_t *>(Y);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i;  // 64 rows x 16 pieces
+            const int row = c >> 4, piece = c & 15;
+            const int m = m0 + row, n = n0 + piece * 8;
+            if (m < M && n < N) {
+                const uint8_t *src = lds + row * kTileBf16Pitch + piece * 16;
+                const u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
+                const u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 8);
+                *reinterpret_cast<u32x4 *>(y + (size_t)m * N + n) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+        }
+        return;
+    }
+    float *y = static_cast<float *>(Y);
+    for (int p = 0; p < 2; ++p) {
+        if (p) __syncthreads();  // the first pass's reads are done
+        if (wm == p) {
+#pragma unroll
+            for (int in = 0; in < 2; ++in) {
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int nl = wn * 64 + in * 32 + 8 * qq + 4 * lh;
+                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(bias_s + nl);
+                    f32x4 v;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = acc[in][0][4 * qq + t] + bv[t];
+                    *reinterpret_cast<f32x4 *>(lds + r32 * kTileF32Pitch + nl * 4) = v;
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + 256 * i;  // 32 rows x 32 pieces
+            const int row = c >> 5, piece = c & 31;
+            const int m = m0 + 32 * p + row, n = n0 + piece * 4;
+            if (m < M && n < N)
+                *reinterpret_cast<u32x4 *>(y + (size_t)m * N + n) =
+                    *reinterpret_cast<const u32x4 *>(lds + row * kTileF32Pitch + piece * 16);
+        }
+    }
+}
+
 }  // namespace svdq

@@ -76,12 +76,16 @@ constexpr int kEpiStore = 0;     // y = acc + T L2 + bias, stored (svdq_w4a4_lin
 constexpr int kEpiPartials = 1;  // int32 group partials stored per group (debug entry point)
 constexpr int kEpiMlp = 2;       // y -> bf16 -> GELU -> the down-projection's activation side
 
-struct Stage6 {
-    uint8_t a[KG * TILE];  // [group][row][48 bytes]
-    uint8_t b[KG * TILE];
+// one LDS stage of a block with kRowsB token rows (128, or 64 in the
+// 64-row tile variant)
+template <int kRowsB>
+struct Stage6T {
+    uint8_t a[KG * TILE];           // [group][row][48 bytes]
+    uint8_t b[KG * kRowsB * GB];
     float sa[KG][BN];
-    float sb[KG][BM];
+    float sb[KG][kRowsB];
 };
+using Stage6 = Stage6T<BM>;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
@@ -305,28 +309,37 @@ __device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t 
     }
 }
 
-template <int kEpi>
-__global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
+// kBMt = 128, or 64 (a 128 x 64 block tile, plain store epilogue only: the
+// same per-wave work for one 32-token slice instead of two, at four blocks
+// per CU instead of three, for shapes whose 128 x 128 tiles leave most
+// block slots of a last round empty)
+template <int kEpi, int kBMt = BM>
+__global__ __launch_bounds__(THREADS, kBMt == BM ? 3 : 4) void w4a4_fp6_kernel(
     const uint8_t *__restrict__ qx, const float *__restrict__ sx, const uint16_t *__restrict__ T,
     const uint8_t *__restrict__ qw, const float *__restrict__ sw, const uint16_t *__restrict__ l2t,
     const uint16_t *__restrict__ bias, int M, int N, int K, int rank, void *__restrict__ Y, bool y_f32,
     int32_t *__restrict__ Pout, int tiles_n, MlpOut mlp) {
     constexpr bool kLinear = kEpi != kEpiPartials;
+    constexpr bool kHalf = kBMt != BM;
+    static_assert(kBMt == BM || (kBMt == 64 && kEpi == kEpiStore), "64-row tiles: plain store epilogue only");
+    constexpr int kTileB = kBMt * GB;    // one group of the block's token rows
+    constexpr int kSlices = kBMt / 64;   // 32-token slices per wave
     // two stages in separate LDS variables: the compiler can then tell the
     // stage being refilled (direct-to-LDS loads) from the one being read and
     // does not make the reads wait for the loads
-    __shared__ __attribute__((aligned(16))) Stage6 st0;
-    __shared__ __attribute__((aligned(16))) Stage6 st1;
+    __shared__ __attribute__((aligned(16))) Stage6T<kBMt> st0;
+    __shared__ __attribute__((aligned(16))) Stage6T<kBMt> st1;
 
     const int tile_n = blockIdx.x % tiles_n;
     const int tile_m = blockIdx.x / tiles_n;
     const int n0 = tile_n * BN;
-    const int m0 = tile_m * BM;
+    const int m0 = tile_m * kBMt;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave & 1;
     const int wm = wave >> 1;
+    const int mw0 = wm * 32 * kSlices;  // the wave's first token row in the block
     const int r32 = lane & 31;
     const int lh = lane >> 5;
     const int G = K / 64;
@@ -339,14 +352,18 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
     const __amdgpu_buffer_rsrc_t rsx = make_rsrc(sx, (uint32_t)G * (uint32_t)M * 4u);
 
     // Per stage the block issues 24 operand loads (per operand and group one
-    // 6 KB tile, six 1 KB loads) and 8 scale loads (side, slot, 64-entry
-    // half); wave w loads tile w (operand w / 2, group w % 2 of the stage)
-    // and scale loads 2w, 2w+1.
+    // 6 KB tile, six 1 KB loads; 3 KB, three loads, for 64 token rows) and 8
+    // scale loads (side, slot, 64-entry half; the token side has one half
+    // with 64 token rows); wave w loads tile w (operand w / 2, group w % 2 of
+    // the stage) and scale loads 2w, 2w+1. A 64-row token tile is the first
+    // or second half of its 128-row container block: each group's 64 rows
+    // are one contiguous 3 KB piece of the block's group tile.
     const int op_w = wave >> 1, q_w = wave & 1;
     const int rows_w = op_w ? M : N;
-    const int b0_w = op_w ? m0 : n0;                     // first row of the 128-row block
-    const uint32_t base_w = (uint32_t)b0_w * R;          // the block's first byte
+    const int b0_w = op_w ? (m0 & ~127) : n0;            // first row of the 128-row block
+    const uint32_t base_w = (uint32_t)b0_w * R + (op_w ? (uint32_t)(m0 - b0_w) * GB : 0u);
     const uint32_t tstride_w = (uint32_t)min(128, rows_w - b0_w) * GB;  // bytes per group in the block
+    const int nld_w = op_w ? kTileB / 1024 : TILE / 1024;  // 1 KB loads per group tile
     uint32_t soff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -362,28 +379,32 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
     // one ds_read2 and needs moves to place each half next to its 16-byte
     // piece in the MFMA operand.
     const int a16 = (wn * 64 + r32) * GB + 16 * lh;
-    const int b16 = (wm * 64 + r32) * GB + 16 * lh;
-    int a8[2], b8[2];
+    const int b16 = (mw0 + r32) * GB + 16 * lh;
+    int a8[2], b8[kSlices];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         a8[i] = (wn * 64 + i * 32 + r32) * GB + 32 + 8 * lh;
-        b8[i] = (wm * 64 + i * 32 + r32) * GB + 32 + 8 * lh;
         asm volatile("" : "+v"(a8[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i) {
+        b8[i] = (mw0 + i * 32 + r32) * GB + 32 + 8 * lh;
         asm volatile("" : "+v"(b8[i]));
     }
 
     // Every offset is carried whole in the per-lane offset, so a load that
     // runs past the end of its buffer is caught by the range check and
     // reads zeros. A group past K is never read and not loaded.
-    auto issue_stage = [&](int s, Stage6 &st) {
+    auto issue_stage = [&](int s, Stage6T<kBMt> &st) {
         const int g = s * KG + q_w;
         if (g < G) {
             const uint32_t t0 = base_w + (uint32_t)g * tstride_w + (uint32_t)lane * 16u;
-            uint8_t *dst = (op_w ? st.b : st.a) + q_w * TILE;
+            uint8_t *dst = op_w ? st.b + q_w * kTileB : st.a + q_w * TILE;
 #pragma unroll
             for (int i = 0; i < 6; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(op_w ? rx : rw, (lds_void *)(dst + i * 1024), 16,
-                                                         t0 + i * 1024, 0, 0, 0);
+                if (i < nld_w)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(op_w ? rx : rw, (lds_void *)(dst + i * 1024), 16,
+                                                             t0 + i * 1024, 0, 0, 0);
         }
         if constexpr (kLinear) {
 #pragma unroll
@@ -393,18 +414,18 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
                 const int gs = s * KG + slot;
                 const uint32_t L = side ? (uint32_t)N : (uint32_t)M;
                 float *dst = (side ? st.sa[slot] : st.sb[slot]) + half * 64;
-                if (gs < G)
+                if (gs < G && (side || half * 64 < kBMt))
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(side ? rsw : rsx, (lds_void *)dst, 4,
                                                              soff[i] + (uint32_t)gs * L * 4u, 0, 0, 0);
             }
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[2][kSlices];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kSlices; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -417,7 +438,7 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
     __syncthreads();
 
     // stage s is read from `cur` while stage s + 1 loads into `nxt`
-    auto run_stage = [&](int s, const Stage6 &cur, Stage6 &nxt) {
+    auto run_stage = [&](int s, const Stage6T<kBMt> &cur, Stage6T<kBMt> &nxt) {
         if (s + 1 < S) issue_stage(s + 1, nxt);
         const int ng = min(KG, G - s * KG);
 #pragma unroll
@@ -434,12 +455,12 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
                 const i32x8 a1 = frag6(cur.a, q * TILE + a16 + 32 * GB, q * TILE + a8[1]);
                 const float swv = cur.sa[q][wn * 64 + lane];
 #pragma unroll
-                for (int im = 0; im < 2; ++im) {
+                for (int im = 0; im < kSlices; ++im) {
                     // keep the scheduler from hoisting the next slice's
                     // operands (and their registers) into this one
                     __builtin_amdgcn_sched_barrier(0);
-                    const i32x8 bm = frag6(cur.b, q * TILE + b16 + im * 32 * GB, q * TILE + b8[im]);
-                    const float sxv = cur.sb[q][wm * 64 + im * 32 + r32];
+                    const i32x8 bm = frag6(cur.b, q * kTileB + b16 + im * 32 * GB, q * kTileB + b8[im]);
+                    const float sxv = cur.sb[q][mw0 + im * 32 + r32];
                     // the slice's MFMAs are issued at raised wave priority
                     // and its FMAs at the normal one (on a SIMD the MFMAs of
                     // one wave and the VALU work of others do not overlap;
@@ -501,40 +522,68 @@ __global__ __launch_bounds__(THREADS, 3) void w4a4_fp6_kernel(
 
     if constexpr (kLinear) {
         for (int kk = 0; kk < rank; kk += 16) {
-            bf16x8 la[2], lb[2];
+            bf16x8 la[2], lb[kSlices];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int n = n0 + wn * 64 + i * 32 + r32;
-                const int m = m0 + wm * 64 + i * 32 + r32;
-                u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
+                u32x4 va = {0u, 0u, 0u, 0u};
                 if (n < N) va = *reinterpret_cast<const u32x4 *>(l2t + (size_t)n * rank + kk + 8 * lh);
-                if (m < M) vb = *reinterpret_cast<const u32x4 *>(T + (size_t)m * rank + kk + 8 * lh);
                 la[i] = __builtin_bit_cast(bf16x8, va);
+            }
+#pragma unroll
+            for (int i = 0; i < kSlices; ++i) {
+                const int m = m0 + mw0 + i * 32 + r32;
+                u32x4 vb = {0u, 0u, 0u, 0u};
+                if (m < M) vb = *reinterpret_cast<const u32x4 *>(T + (size_t)m * rank + kk + 8 * lh);
                 lb[i] = __builtin_bit_cast(bf16x8, vb);
             }
 #pragma unroll
             for (int in = 0; in < 2; ++in)
 #pragma unroll
-                for (int im = 0; im < 2; ++im) acc[in][im] = mfma_bf16_32x32x16(la[in], lb[im], acc[in][im]);
+                for (int im = 0; im < kSlices; ++im) acc[in][im] = mfma_bf16_32x32x16(la[in], lb[im], acc[in][im]);
         }
         // every load has landed and been read: the stage buffers hold the
         // output tile on its way out
-        static_assert(sizeof(Stage6) >= kTileHalfLdsBytes, "LDS too small for the output tile");
-        static_assert(sizeof(Stage6) >= kMlpLdsBytes, "LDS too small for the MLP epilogue");
-        if constexpr (kEpi == kEpiMlp)
-            mlp_epilogue(acc, reinterpret_cast<uint8_t *>(&st0), bias_s, mlp, M, N, m0, n0, tile_n, wn, wm, tid);
-        else
-            store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&st0), reinterpret_cast<uint8_t *>(&st1), bias_s, Y,
-                               y_f32, M, N, m0, n0, wn, wm, tid);
+        if constexpr (kHalf) {
+            static_assert(sizeof(Stage6T<kBMt>) >= kTile64LdsBytes, "LDS too small for the output tile");
+            store_tile_128x64(acc, reinterpret_cast<uint8_t *>(&st0), bias_s, Y, y_f32, M, N, m0, n0, wn, wm, tid);
+        } else {
+            static_assert(sizeof(Stage6) >= kTileHalfLdsBytes, "LDS too small for the output tile");
+            static_assert(sizeof(Stage6) >= kMlpLdsBytes, "LDS too small for the MLP epilogue");
+            if constexpr (kEpi == kEpiMlp)
+                mlp_epilogue(acc, reinterpret_cast<uint8_t *>(&st0), bias_s, mlp, M, N, m0, n0, tile_n, wn, wm, tid);
+            else
+                store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&st0), reinterpret_cast<uint8_t *>(&st1),
+                                   bias_s, Y, y_f32, M, N, m0, n0, wn, wm, tid);
+        }
     }
 }
 
 }  // namespace
 
+static bool fp6_use_64_row_tiles(int M, int N) {
+    // The kernel is bound by its per-SIMD MFMA and VALU work, so a CU's time
+    // follows the tile work it is dealt: 128 x 128 tiles at three blocks per
+    // CU, or 128 x 64 tiles (half the work each) at four. Dealt round-robin
+    // over kCUs CUs, the busiest CU gets ceil(tiles / kCUs) tiles; the
+    // 64-row tiles are used when that is at least 10 % less work.
+    constexpr int64_t kCUs = 256;  // MI355X
+    const int64_t tn = (N + BN - 1) / BN;
+    const int64_t full = (tn * ((M + BM - 1) / BM) + kCUs - 1) / kCUs;    // 128 x 128 tiles
+    const int64_t half = (tn * ((M + 63) / 64) + kCUs - 1) / kCUs;        // 128 x 64 tiles
+    return 10 * half < 9 * 2 * full;
+}
+
 hipError_t launch_w4a4_fp6_linear(const uint8_t *qx, const float *sx, const uint16_t *T, const uint8_t *qw,
                                   const float *sw, const uint16_t *l2t, const uint16_t *bias, int M, int N,
                                   int K, int rank, void *Y, bool y_f32, hipStream_t stream) {
     const int tiles_n = (N + BN - 1) / BN;
+    if (fp6_use_64_row_tiles(M, N)) {
+        const int tiles_m = (M + 63) / 64;
+        hipLaunchKernelGGL((w4a4_fp6_kernel<kEpiStore, 64>), dim3(tiles_n * tiles_m), dim3(THREADS), 0, stream, qx,
+                           sx, T, qw, sw, l2t, bias, M, N, K, rank, Y, y_f32, nullptr, tiles_n, MlpOut{});
+        return hipGetLastError();
+    }
     const int tiles_m = (M + BM - 1) / BM;
     hipLaunchKernelGGL(w4a4_fp6_kernel<kEpiStore>, dim3(tiles_n * tiles_m), dim3(THREADS), 0, stream, qx, sx, T,
                        qw, sw, l2t, bias, M, N, K, rank, Y, y_f32, nullptr, tiles_n, MlpOut{});
