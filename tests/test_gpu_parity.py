@@ -221,10 +221,10 @@ def test_w4a4_linear_tiny(out, qfmt):
 
 # The FP6 GEMM runs 128 x 64 block tiles when they spread the work over the
 # CUs markedly better than 128 x 128 ones: small shapes take the 64-row
-# tiles; (200, 128, 16384, 16), whose 256 tiles of 128 x 128 fill the CUs
-# exactly, keeps the 128-row tiles with a ragged last row tile.
+# tiles; (200, 128, 32768, 16), whose 512 tiles of 128 x 128 fill the 256
+# CUs exactly twice, keeps the 128-row tiles with a ragged last row tile.
 @pytest.mark.parametrize("shape", [(77, 320, 200, 16), (1, 64, 16, 16), (257, 512, 136, 32), (130, 256, 264, 0),
-                                   (65, 128, 384, 64), (300, 256, 520, 32), (200, 128, 16384, 16)])
+                                   (65, 128, 384, 64), (300, 256, 520, 32), (200, 128, 32768, 16)])
 @pytest.mark.parametrize("qfmt", H.FORMATS, ids=H.FORMAT_IDS)
 def test_w4a4_linear_ragged(shape, qfmt):
     M, K, N, r = shape
