@@ -63,7 +63,7 @@ CSRC = os.path.join(ROOT, "bit_quantized_linear_amd", "csrc")
 GEMM_SOURCES = ("w4a4_fp6_gemm.hip", "device_common.h", "quant_common.h", "gelu.h")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "svdq_w4a4_linear_fp6_mlp_up_4608x3072x12288_traffic.txt")
 COPY_BYTES = 256 << 20  # calibration kernel: reads and writes this many bytes
-GEMM_KERNEL_KEY = "w4a4_fp6_kernel<0>"
+GEMM_KERNEL_KEY = "w4a4_fp6_kernel<0, 128>"
 COPY_KERNEL_KEY = "neg_kernel"
 W16_SOURCES = ("w4a16.hip", "device_common.h")
 W16_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "w4a16_linear_modulation_2x3072x18432_traffic.txt")
@@ -173,7 +173,7 @@ def summarize_pmc(fetch_dir, write_dir, which="fp6_gemm"):
 # hash the summary records, the workload, and the MFMA operations one launch
 # must perform (with the counter that counts them), or None.
 COUNTER_KERNELS = {
-    "fp6_gemm": ("w4a4_fp6_kernel<0>", GEMM_SOURCES,
+    "fp6_gemm": (GEMM_KERNEL_KEY, GEMM_SOURCES,
                  "svdq_w4a4_linear (FP6 container), mlp_up M=4608 K=3072 N=12288 rank=32",
                  2 * 4608 * 3072 * 12288, "SQ_INSTS_VALU_MFMA_MOPS_F6F4"),
     "int4_gemm": ("w4a4_gemm_kernel", ("w4a4_gemm.hip", "gemm_int.h", "device_common.h"),
