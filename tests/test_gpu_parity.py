@@ -264,11 +264,16 @@ def test_w4a4_attention_projection_full(qfmt):
         rel_l2(ref["y64"], X["values"].astype(F64) @ W["values"].astype(F64) + bias["values"]))
 
 
+# the oracle's preparation of a full-size case (40 s for the video case),
+# shared by the tests of both containers and the one-GPU share below
+prepared_full = functools.lru_cache(maxsize=1)(H.prepared_case)
+
+
 @functools.lru_cache(maxsize=1)
 def full_reference(name):
     """The oracle's whole forward of a named full-size case (main product in
     its dense closed form), shared by the tests of both containers."""
-    case, X, W, bias, prep, abi = H.prepared_case(name)
+    case, X, W, bias, prep, abi = prepared_full(name)
     say("  oracle forward", name, (case.M, case.K, case.N))
     return sq.forward_dense(X["values"], prep, bias["values"], "bf16")
 
@@ -279,7 +284,7 @@ def test_w4a4_full_size_every_row(name, qfmt):
     """Full-size shapes in the launch configuration the bench times (the
     activation pass with its workspace, then the GEMM): every code, scale and
     T element, and every output element against the oracle's whole forward."""
-    case, X, W, bias, prep, abi = H.prepared_case(name)
+    case, X, W, bias, prep, abi = prepared_full(name)
     M, K, N, r = case.M, case.K, case.N, case.rank
     say("linear full-size", name, (M, K, N, r), qfmt)
     qx, sx, T = H.run_quantize_act(X["bits"], abi, r, qfmt)
@@ -291,6 +296,28 @@ def test_w4a4_full_size_every_row(name, qfmt):
     y = sq.bf16_from_bits(H.host(Y).view(np.uint16))
     del Y
     check_w4a4(y, ref, prep, bias["values"], "bf16", Tv, what=f"{name} {qfmt}")
+
+
+@pytest.mark.parametrize("qfmt", H.FORMATS, ids=H.FORMAT_IDS)
+def test_w4a4_video_one_gpu_share(qfmt):
+    """One GPU's share of the video linear under token (row) parallelism over
+    8 GPUs: the first 4095 of its 32760 tokens (15 * 256 + 255 rows, a ragged
+    last row tile) through the weights prepared for the whole workload, with
+    the activation pass's workspace as the bench launches it; every code,
+    scale and T element and every output element against the oracle."""
+    case, X, W, bias, prep, abi = prepared_full("video")
+    M, K, N, r = 4095, case.K, case.N, case.rank
+    say("linear one GPU's share of video", (M, K, N, r), qfmt)
+    Xb = np.ascontiguousarray(X["bits"][:M])
+    Xv = X["values"][:M]
+    qx, sx, T = H.run_quantize_act(Xb, abi, r, qfmt)
+    Y = H.run_linear(qx, sx, T, abi, bias["bits"], M, N, K, r, "bf16", qfmt, H.weights_bytes(prep, abi, qfmt))
+    ref = sq.forward_dense(Xv, prep, bias["values"], "bf16")
+    assert np.array_equal(H.unpack_codes(H.host(qx), K, qfmt), ref["qx"])
+    assert np.array_equal(H.host(sx), ref["sx"])
+    Tv = check_T(T, ref["T"], Xv, prep["L1s"])
+    y = sq.bf16_from_bits(H.host(Y).view(np.uint16))
+    check_w4a4(y, ref, prep, bias["values"], "bf16", Tv, what=f"video share {qfmt}")
 
 
 def test_library_prepared_chain_mlp_up():
