@@ -72,7 +72,14 @@ __device__ __forceinline__ void pack_fp6_16(const float (&v)[16], uint32_t (&w)[
         a[i] = v[2 * i];
         b[i] = v[2 * i + 1];
     }
-    const auto r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 1.0f);
+    auto r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 1.0f);
+    // Both operands stay live until after the conversion (an empty asm
+    // statement that reads them and passes the result through, so it cannot
+    // move above the conversion): its result is then never given registers
+    // of an operand. With the result starting on the second operand's third
+    // register (v[16:21] over v[14:29]) the instruction packed a 0 for that
+    // value.
+    asm volatile("" : "+v"(r) : "v"(a), "v"(b));
 #pragma clang diagnostic pop
     w[0] = r[0];
     w[1] = r[1];

@@ -121,7 +121,8 @@ constexpr int kMlpLdsBytes = kMlpTabOff + kGeluTableEntries * 2;
 // tile's 128 rows of L1s (16x16x32 bf16 MFMAs, fp32 accumulation) and
 // stores the fp32 partial of T for this column tile. Columns past N (N is
 // a multiple of 64, so a whole group) give g = 0 and are not written.
-__device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t *lds, const float *bias_s,
+__device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t *lds, uint8_t *lds_hi,
+                                             const float *bias_s,
                                              const MlpOut &o, int M, int N,
                                              int m0, int n0, int tile_n, int wn, int wm, int tid) {
     const int lane = tid & 63, r32 = lane & 31, lh = lane >> 5;
@@ -141,30 +142,30 @@ __device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t 
     const bool grp_ok = n0 + 64 * gl < N;
     const int nb = min(128, M - m0);  // rows of this block of the container
     const int g_down = 2 * (n0 / 128) + gl;
-    for (int p = 0; p < 2; ++p) {
-        if (wm == p) {
+    // the whole y tile into LDS first (rows 0..63 in lds, 64..127 in
+    // lds_hi), so that the accumulators are dead before the quantizer runs
 #pragma unroll
-            for (int in = 0; in < 2; ++in) {
+    for (int in = 0; in < 2; ++in) {
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const int nl = wn * 64 + in * 32 + 8 * qq + 4 * lh;
-                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(bias_s + nl);
+        for (int qq = 0; qq < 4; ++qq) {
+            const int nl = wn * 64 + in * 32 + 8 * qq + 4 * lh;
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(bias_s + nl);
 #pragma unroll
-                    for (int im = 0; im < 2; ++im) {
-                        const int ml = im * 32 + r32;
-                        float v[4];
+            for (int im = 0; im < 2; ++im) {
+                const int ml = im * 32 + r32;
+                float v[4];
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * qq + t] + bv[t];
-                        *reinterpret_cast<u32x2 *>(lds + ml * kMlpPitch + nl * 2) =
-                            u32x2{bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
-                    }
-                }
+                for (int t = 0; t < 4; ++t) v[t] = acc[in][im][4 * qq + t] + bv[t];
+                *reinterpret_cast<u32x2 *>((wm ? lds_hi : lds) + ml * kMlpPitch + nl * 2) =
+                    u32x2{bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
             }
         }
-        __syncthreads();
-
+    }
+    __syncthreads();
+    for (int p = 0; p < 2; ++p) {
+        uint8_t *tile = p ? lds_hi : lds;
         const int m = m0 + 64 * p + row;
-        uint8_t *rowp = lds + row * kMlpPitch + 64 * qd;
+        uint8_t *rowp = tile + row * kMlpPitch + 64 * qd;
         uint32_t w[16];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -188,10 +189,10 @@ __device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t 
 #pragma unroll
         for (int i = 0; i < 8; ++i) reinterpret_cast<u32x2 *>(rowp)[i] = u32x2{w[2 * i], w[2 * i + 1]};
 
-        // x_hat = fp32(g / s): exact through fp64 reciprocals (quotient_fp32).
-        // One sweep for the group absmax, a second one recomputes x_hat for
-        // the codes; both read g and 1 / s back from LDS eight channels at a
-        // time (cheaper in registers than holding 32 quotients)
+        // x_hat = fp32(g / s): exact through fp64 reciprocals (quotient_fp32),
+        // computed once (g and 1 / s read back from LDS eight channels at a
+        // time) and held for the codes: the main loop's registers are free
+        // by now
         auto chunk = [&](int c, float gv[8]) {
             // rows are 8-byte aligned (264-byte pitch): two 8-byte reads
             const u32x2 x0 = reinterpret_cast<const u32x2 *>(rowp)[2 * c];
@@ -204,12 +205,16 @@ __device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t 
             }
         };
         float amax = 0.0f;
-#pragma unroll 1
+        float xq[32];
+#pragma unroll
         for (int c = 0; c < 4; ++c) {
             float gv[8];
             chunk(c, gv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(quotient_fp32(gv[i], rcp[32 * qd + 8 * c + i])));
+            for (int i = 0; i < 8; ++i) {
+                xq[8 * c + i] = quotient_fp32(gv[i], rcp[32 * qd + 8 * c + i]);
+                amax = fmaxf(amax, fabsf(xq[8 * c + i]));
+            }
         }
         amax = fmaxf(amax, __shfl_xor(amax, 1));
         // below the range quotient_fp32 covers: IEEE divisions (both threads
@@ -237,17 +242,18 @@ __device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t 
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 float v[16];
+                if (tiny) {
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const int c = 2 * hh + cc;
-                    float gv[8];
-                    chunk(c, gv);
+                    for (int cc = 0; cc < 2; ++cc) {
+                        const int c = 2 * hh + cc;
+                        float gv[8];
+                        chunk(c, gv);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float xh = tiny ? gv[i] / sv[32 * qd + 8 * c + i]
-                                              : quotient_fp32(gv[i], rcp[32 * qd + 8 * c + i]);
-                        v[8 * cc + i] = fp6_value(xh, rscale);
+                        for (int i = 0; i < 8; ++i) v[8 * cc + i] = fp6_value(gv[i] / sv[32 * qd + 8 * c + i], rscale);
                     }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) v[i] = fp6_value(xq[16 * hh + i], rscale);
                 }
                 uint32_t w3[3];
                 pack_fp6_16(v, w3);
@@ -276,7 +282,7 @@ __device__ __forceinline__ void mlp_epilogue(const f32x16 (&acc)[2][2], uint8_t 
 #pragma unroll
             for (int step = 0; step < 4; ++step) {
                 const int kc = 32 * step + 8 * (lane >> 4);
-                const uint8_t *ap = lds + ar * kMlpPitch + kc * 2;
+                const uint8_t *ap = tile + ar * kMlpPitch + kc * 2;
                 const u32x2 a0 = reinterpret_cast<const u32x2 *>(ap)[0];
                 const u32x2 a1 = reinterpret_cast<const u32x2 *>(ap)[1];
                 const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
@@ -551,7 +557,8 @@ __global__ __launch_bounds__(THREADS, kBMt == BM ? 3 : 4) void w4a4_fp6_kernel(
             static_assert(sizeof(Stage6) >= kTileHalfLdsBytes, "LDS too small for the output tile");
             static_assert(sizeof(Stage6) >= kMlpLdsBytes, "LDS too small for the MLP epilogue");
             if constexpr (kEpi == kEpiMlp)
-                mlp_epilogue(acc, reinterpret_cast<uint8_t *>(&st0), bias_s, mlp, M, N, m0, n0, tile_n, wn, wm, tid);
+                mlp_epilogue(acc, reinterpret_cast<uint8_t *>(&st0), reinterpret_cast<uint8_t *>(&st1), bias_s, mlp, M,
+                             N, m0, n0, tile_n, wn, wm, tid);
             else
                 store_tile_128x128(acc, reinterpret_cast<uint8_t *>(&st0), reinterpret_cast<uint8_t *>(&st1),
                                    bias_s, Y, y_f32, M, N, m0, n0, wn, wm, tid);
