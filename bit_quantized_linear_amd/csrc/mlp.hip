@@ -19,24 +19,34 @@ namespace svdq {
 namespace {
 
 // T[m, j] = bf16(sum over column tiles c, in ascending order, of
-// tpart[c, m, j]): one thread per element, deterministic.
+// tpart[c, m, j]): deterministic. Each thread sums four consecutive elements
+// (16-byte loads of the partials, one 8-byte store of T; n = M * rank is a
+// multiple of 16 and the workspace 16-byte aligned), or one where T is not
+// 8-byte aligned.
+template <int kVec>
 __global__ __launch_bounds__(256) void tpart_reduce_kernel(const float *__restrict__ tpart, int parts, int M,
                                                            int rank, uint16_t *__restrict__ T) {
+    typedef float fv __attribute__((ext_vector_type(kVec)));
     const size_t n = (size_t)M * rank;
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * kVec;
     if (i >= n) return;
     // loads eight partials ahead of the adds (the adds stay in order)
-    float v = 0.0f;
+    fv v = {};
     int c = 0;
     for (; c + 8 <= parts; c += 8) {
-        float p[8];
+        fv p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = tpart[(size_t)(c + j) * n + i];
+        for (int j = 0; j < 8; ++j) p[j] = *reinterpret_cast<const fv *>(tpart + (size_t)(c + j) * n + i);
 #pragma unroll
         for (int j = 0; j < 8; ++j) v += p[j];
     }
-    for (; c < parts; ++c) v += tpart[(size_t)c * n + i];
-    T[i] = (uint16_t)f32_to_bf16_bits(v);
+    for (; c < parts; ++c) v += *reinterpret_cast<const fv *>(tpart + (size_t)c * n + i);
+    if constexpr (kVec == 4) {
+        *reinterpret_cast<u32x2 *>(T + i) = u32x2{f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                                                  f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
+    } else {
+        T[i] = (uint16_t)f32_to_bf16_bits(v[0]);
+    }
 }
 
 // Elementwise GELU: each block loads the table into LDS once and handles
@@ -76,8 +86,14 @@ __global__ __launch_bounds__(256) void gelu_bf16_kernel(const uint16_t *__restri
 hipError_t launch_tpart_reduce(const float *tpart, int parts, int M, int rank, uint16_t *T, hipStream_t stream) {
     const size_t n = (size_t)M * rank;
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(tpart_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, tpart, parts,
-                       M, rank, T);
+    if ((n % 4) == 0 && (reinterpret_cast<uintptr_t>(T) & 7u) == 0 && (reinterpret_cast<uintptr_t>(tpart) & 15u) == 0) {
+        const size_t threads = n / 4;
+        hipLaunchKernelGGL(tpart_reduce_kernel<4>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                           tpart, parts, M, rank, T);
+    } else {
+        hipLaunchKernelGGL(tpart_reduce_kernel<1>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, tpart,
+                           parts, M, rank, T);
+    }
     return hipGetLastError();
 }
 
