@@ -23,8 +23,11 @@
 // output element and group.
 //
 // Block tile 128 (n) x 128 (m), 4 waves as 2 x 2, wave tile 64 x 64 (2 x 2
-// MFMA tiles of 32 x 32). One LDS stage holds two groups (K = 128): per
-// operand the two groups' [128 rows][48 bytes] tiles, exactly as the FP6
+// MFMA tiles of 32 x 32); for shapes whose 128 x 128 tiles would leave a
+// last round of block slots mostly empty, 128 x 64 (wave tile 64 x 32, four
+// blocks per CU; the plain store epilogue only). One LDS stage holds two
+// groups (K = 128): per operand the two groups' [128 rows][48 bytes] tiles
+// (64 token rows in the 128 x 64 tile), exactly as the FP6
 // container stores them (rows in blocks of 128, each block's groups one after
 // another), plus the two groups' 2 x 128 scales. Operands and scales go
 // straight from global memory to LDS (buffer_load ... lds, 16 or 4 bytes per
