@@ -102,21 +102,24 @@ __device__ __forceinline__ i32x8 frag6(const uint8_t *region, int off16, int off
     return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], 0, 0};
 }
 
-// LDS of the MLP epilogue (the stage buffers are free by then): a bf16 tile
-// of 64 rows x 128 columns (rows padded to 264 bytes), 1 / s and s of the
-// tile's 128 channels, and the GELU table.
+// LDS of the MLP epilogue (the stage buffers are free by then): in the
+// first stage buffer a bf16 tile of 64 rows x 128 columns (rows padded to
+// 264 bytes), 1 / s and s of the tile's 128 channels, and the GELU table;
+// in the second the tile's other 64 rows at the same pitch.
 constexpr int kMlpPitch = 264;
 constexpr int kMlpRcpOff = 64 * kMlpPitch;
 constexpr int kMlpSOff = kMlpRcpOff + 128 * 8;
 constexpr int kMlpTabOff = kMlpSOff + 128 * 4;
 constexpr int kMlpLdsBytes = kMlpTabOff + kGeluTableEntries * 2;
 
-// The tile's y = acc + bias, in two passes of 64 token rows (the waves of
-// one wm row write their accumulators, rounded to bf16, into the LDS tile).
-// Then thread t takes row t / 4 and the 32 channels 32 (t % 4) of it:
+// The tile's y = acc + bias, rounded to bf16, goes into LDS whole (rows
+// 0..63 in lds, 64..127 in lds_hi), so the accumulators are dead before the
+// quantizer runs. Then in two passes of 64 token rows, thread t takes row
+// t / 4 and the 32 channels 32 (t % 4) of it:
 // (optionally) stores y_up, replaces y by g = GELU(y) in the tile, and
-// quantizes g as the standalone activation pass does: x_hat = fp32(g / s),
-// the group absmax over its 32 channels and the partner thread's (t ^ 1,
+// quantizes g as the standalone activation pass does: x_hat = fp32(g / s)
+// (computed once, held in registers), the group absmax over its 32
+// channels and the partner thread's (t ^ 1,
 // the other half of the group), scale = absmax / 7, codes by nearest even,
 // written as FP6 fields straight into the down-projection's container (the
 // tile's rows are one 128-row block of it, its 128 columns two groups).
