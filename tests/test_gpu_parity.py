@@ -519,7 +519,9 @@ def test_empty_batch_is_a_no_op():
 
 # ---------------------------------------------------------------- W8A8 ---
 
-@pytest.mark.parametrize("shape", [(64, 256, 256), (77, 192, 136), (1, 64, 8)])
+# K = 576 is five 128-byte stages, the last one half (the GEMM runs stages
+# in pairs and the odd one after them)
+@pytest.mark.parametrize("shape", [(64, 256, 256), (77, 192, 136), (1, 64, 8), (200, 576, 264)])
 def test_w8a8_small(shape):
     M, K, N = shape
     say("w8a8", shape)
@@ -564,7 +566,7 @@ def test_w8a8_full_shapes(name):
     check_w8a8(H.y_values(Y, "bf16"), ref, sw, bias["values"], name)
 
 
-@pytest.mark.parametrize("shape", [(64, 256, 256), (130, 320, 136)])
+@pytest.mark.parametrize("shape", [(64, 256, 256), (130, 320, 136), (200, 576, 264)])
 def test_w8a8_accumulators_bit_exact(shape):
     M, K, N = shape
     say("w8a8 acc", shape)
