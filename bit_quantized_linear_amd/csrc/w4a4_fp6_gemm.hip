@@ -364,25 +364,32 @@ __global__ __launch_bounds__(THREADS, kBMt == BM ? 3 : 4) void w4a4_fp6_kernel(
     const __amdgpu_buffer_rsrc_t rsx = make_rsrc(sx, (uint32_t)G * (uint32_t)M * 4u);
 
     // Per stage the block issues 24 operand loads (per operand and group one
-    // 6 KB tile, six 1 KB loads; 3 KB, three loads, for 64 token rows) and 8
-    // scale loads (side, slot, 64-entry half; the token side has one half
-    // with 64 token rows); wave w loads tile w (operand w / 2, group w % 2 of
-    // the stage) and scale loads 2w, 2w+1. A 64-row token tile is the first
-    // or second half of its 128-row container block: each group's 64 rows
-    // are one contiguous 3 KB piece of the block's group tile.
+    // 6 KB tile, six 1 KB loads; 3 KB, three loads, for 64 token rows); wave
+    // w loads tile w (operand w / 2, group w % 2 of the stage). A 64-row
+    // token tile is the first or second half of its 128-row container block:
+    // each group's 64 rows are one contiguous 3 KB piece of the block's group
+    // tile. The stage's scales of one side are two runs of 4 bytes per row
+    // (one per group) in memory and one [2][rows] array in LDS: with four
+    // rows per lane, one 16-byte load per side puts both runs in place
+    // (wave 2 the weight side, wave 3 the token side). That needs the runs
+    // to start on 16 bytes, i.e. a row count that is a multiple of 4 (N
+    // always is; for M % 4 != 0 the token side takes four 4-byte loads, one
+    // per group and 64-row half, by waves 2 and 3). A lane's 16 bytes then
+    // lie wholly inside or wholly past the end of the buffer.
     const int op_w = wave >> 1, q_w = wave & 1;
     const int rows_w = op_w ? M : N;
     const int b0_w = op_w ? (m0 & ~127) : n0;            // first row of the 128-row block
     const uint32_t base_w = (uint32_t)b0_w * R + (op_w ? (uint32_t)(m0 - b0_w) * GB : 0u);
     const uint32_t tstride_w = (uint32_t)min(128, rows_w - b0_w) * GB;  // bytes per group in the block
     const int nld_w = op_w ? kTileB / 1024 : TILE / 1024;  // 1 KB loads per group tile
-    uint32_t soff[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int idx = wave * 2 + i;
-        const int side = idx / 4, half = idx % 2;
-        soff[i] = (uint32_t)((side ? n0 : m0) + half * 64 + lane) * 4u;
-    }
+    const bool sx16 = (M & 3) == 0;
+    // the lane's scale piece: side (1: weights), its group within the stage
+    // and its byte offset within that group's run
+    const int s_side = wave == 2;
+    const int s_per = s_side ? BN / 4 : kBMt / 4;  // lanes per group
+    const bool s_lane = wave >= 2 && lane < 2 * s_per;
+    const int s_slot = lane / s_per;
+    const uint32_t s_off = (uint32_t)((s_side ? n0 : m0) + 4 * (lane % s_per)) * 4u;
     // byte offsets of this lane's operand pieces within a staged operand:
     // row r's 16-byte piece of plane lh at r * 48 + 16 lh, its 8-byte piece
     // of plane 2 at r * 48 + 32 + 8 lh; tile i (rows + 32 i) and slot q
@@ -419,16 +426,24 @@ __global__ __launch_bounds__(THREADS, kBMt == BM ? 3 : 4) void w4a4_fp6_kernel(
                                                              t0 + i * 1024, 0, 0, 0);
         }
         if constexpr (kLinear) {
+            if (sx16 || s_side) {
+                // a group past G lies past the end of the buffer: zeros, never read
+                const uint32_t L = s_side ? (uint32_t)N : (uint32_t)M;
+                if (s_lane)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_side ? rsw : rsx,
+                                                             (lds_void *)(s_side ? &st.sa[0][0] : &st.sb[0][0]), 16,
+                                                             (uint32_t)(s * KG + s_slot) * L * 4u + s_off, 0, 0, 0);
+            }
+            if (!sx16 && wave >= 2) {
+                // token scales 4 bytes per lane: wave 2 group 0, wave 3 group
+                // 1 of the stage, each in 64-row halves
+                const int slot = wave - 2, gs = s * KG + slot;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int idx = wave * 2 + i;
-                const int side = idx / 4, slot = (idx % 4) / 2, half = idx % 2;
-                const int gs = s * KG + slot;
-                const uint32_t L = side ? (uint32_t)N : (uint32_t)M;
-                float *dst = (side ? st.sa[slot] : st.sb[slot]) + half * 64;
-                if (gs < G && (side || half * 64 < kBMt))
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(side ? rsw : rsx, (lds_void *)dst, 4,
-                                                             soff[i] + (uint32_t)gs * L * 4u, 0, 0, 0);
+                for (int half = 0; half < kBMt / 64; ++half)
+                    if (gs < G)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rsx, (lds_void *)(st.sb[slot] + half * 64), 4,
+                            ((uint32_t)gs * (uint32_t)M + (uint32_t)(m0 + half * 64 + lane)) * 4u, 0, 0, 0);
             }
         }
     };
