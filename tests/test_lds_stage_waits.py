@@ -4,7 +4,7 @@ from the one being read. With the stages in one array, in a kernel with
 more than one LDS variable, it put a wait for every outstanding load
 (`s_waitcnt vmcnt(0)`) between a stage's refill loads and its first LDS
 read, so each stage waited for loads it had just issued. This compiles the
-three kernels to gfx950 assembly (host only, no GPU) and checks that no wait
+four kernels to gfx950 assembly (host only, no GPU) and checks that no wait
 that needs one of a stage's direct-to-LDS loads to have landed sits between
 those loads and the next LDS read unless a barrier separates them (the
 intended waits come right before the barrier that ends a stage, or the one
@@ -20,7 +20,7 @@ import pytest
 
 from bit_quantized_linear_amd import build as B
 
-SOURCES = ["w4a4_fp6_gemm.hip", "mx_gemm.hip", "w8a8.hip"]
+SOURCES = ["w4a4_fp6_gemm.hip", "w4a4_gemm.hip", "mx_gemm.hip", "w8a8.hip"]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(B.HIPCC) or shutil.which("python3") is None,
                                 reason="hipcc not available")
