@@ -176,14 +176,14 @@ COUNTER_KERNELS = {
     "fp6_gemm": (GEMM_KERNEL_KEY, GEMM_SOURCES,
                  "svdq_w4a4_linear (FP6 container), mlp_up M=4608 K=3072 N=12288 rank=32",
                  2 * 4608 * 3072 * 12288, "SQ_INSTS_VALU_MFMA_MOPS_F6F4"),
-    "int4_gemm": ("w4a4_gemm_kernel", ("w4a4_gemm.hip", "gemm_int.h", "device_common.h"),
+    "int4_gemm": ("w4a4_int4_kernel", ("w4a4_gemm.hip", "device_common.h"),
                   "svdq_w4a4_linear (INT4 container), mlp_up M=4608 K=3072 N=12288 rank=32",
                   2 * 4608 * 3072 * 12288, "SQ_INSTS_VALU_MFMA_MOPS_I8"),
     "act": ("quantize_act_kernel<1, 2>", ("act_quant.hip", "quant_common.h", "device_common.h"),
             "svdq_quantize_act (FP6 container), mlp_up M=4608 K=3072 rank=32", None, None),
     "mx_gemm": (MX_KERNEL_KEY, MX_SOURCES, "svdq_mx_linear (MXFP4), mlp_up M=4608 K=3072 N=12288 rank=32",
                 2 * 4608 * 3072 * 12288, "SQ_INSTS_VALU_MFMA_MOPS_F6F4"),
-    "w8a8_gemm": ("w8a8_gemm256_kernel", ("w8a8.hip", "gemm_int.h", "device_common.h", "quant_common.h"),
+    "w8a8_gemm": ("w8a8_gemm256_kernel", ("w8a8.hip", "device_common.h", "quant_common.h"),
                   "w8a8_linear GEMM, attention projection M=4608 K=3072 N=3072",
                   2 * 4608 * 3072 * 3072, "SQ_INSTS_VALU_MFMA_MOPS_I8"),
 }
