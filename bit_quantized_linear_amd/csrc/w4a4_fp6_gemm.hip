@@ -373,9 +373,9 @@ __global__ __launch_bounds__(THREADS, kBMt == BM ? 3 : 4) void w4a4_fp6_kernel(
     // rows per lane, one 16-byte load per side puts both runs in place
     // (wave 2 the weight side, wave 3 the token side). That needs the runs
     // to start on 16 bytes, i.e. a row count that is a multiple of 4 (N
-    // always is; for M % 4 != 0 the token side takes four 4-byte loads, one
-    // per group and 64-row half, by waves 2 and 3). A lane's 16 bytes then
-    // lie wholly inside or wholly past the end of the buffer.
+    // always is; for M % 4 != 0 the token side takes one 4-byte load per
+    // group and 64-row half, by waves 2 and 3). A lane's 16 bytes then lie
+    // wholly inside or wholly past the end of the buffer.
     const int op_w = wave >> 1, q_w = wave & 1;
     const int rows_w = op_w ? M : N;
     const int b0_w = op_w ? (m0 & ~127) : n0;            // first row of the 128-row block
