@@ -250,6 +250,28 @@ def test_w4a4_linear_no_bias_zero_rows(qfmt):
     assert np.all(y[[0, 7, 39]] == 0.0)
 
 
+# The two containers hold the same codes, and their kernels apply the same
+# arithmetic in the same order (the INT4 one on 256 times each partial, which
+# a power-of-two factor leaves exact in fp32 while the accumulator is a
+# normal number), so their outputs agree byte for byte. The shapes take both
+# FP6 tile heights and both scale-load paths of each kernel (token counts
+# that are and are not multiples of 4).
+@pytest.mark.parametrize("shape", [(77, 320, 200, 16), (300, 256, 520, 32), (260, 3072, 3072, 32),
+                                   (200, 128, 32768, 16), (1023, 256, 8192, 16)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_containers_give_identical_outputs(shape, out):
+    M, K, N, r = shape
+    say("containers agree", shape, out)
+    p = H.make_problem(M, K, N, r, seed=M + N, outliers=(1,), zero_rows=(M - 1,))
+    ys = []
+    for qfmt in H.FORMATS:
+        qx, sx, T = H.run_quantize_act(p["X"]["bits"], p["abi"], r, qfmt)
+        Y = H.run_linear(qx, sx, T, p["abi"], p["bias"]["bits"], M, N, K, r, out, qfmt,
+                         H.weights_bytes(p["prep"], p["abi"], qfmt))
+        ys.append(H.host(Y).view(np.uint8))
+    assert np.array_equal(ys[0], ys[1])
+
+
 @pytest.mark.parametrize("qfmt", H.FORMATS, ids=H.FORMAT_IDS)
 def test_w4a4_attention_projection_full(qfmt):
     case, X, W, bias, prep, abi = H.prepared_case("attn_proj")
