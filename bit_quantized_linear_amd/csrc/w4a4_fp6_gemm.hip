@@ -489,10 +489,10 @@ __global__ __launch_bounds__(THREADS, kBMt == BM ? 3 : 4) void w4a4_fp6_kernel(
                     const i32x8 bm = frag6(cur.b, q * kTileB + b16 + im * 32 * GB, q * kTileB + b8[im]);
                     const float sxv = cur.sb[q][mw0 + im * 32 + r32];
                     // the slice's MFMAs are issued at raised wave priority
-                    // and its FMAs at the normal one (on a SIMD the MFMAs of
-                    // one wave and the VALU work of others do not overlap;
-                    // letting the waves that are ready for the matrix core go
-                    // first measured 2 % faster)
+                    // and its FMAs at the normal one, so that waves ready
+                    // for the matrix core go first (2 % faster in an earlier
+                    // form of this loop; no measurable difference, either
+                    // way, in this one)
                     __builtin_amdgcn_s_setprio(1);
                     const f32x32 C = __builtin_amdgcn_mfma_f32_32x32x1f32(swv, sxv, zero32, 0, 0, 0);
                     const f32x16 P0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bm, zero16, 2, 2, 0,
